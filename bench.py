@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP4 linear-layer hot path on one MI355X.
+
+One step = rotate + quantize operand A, rotate + quantize operand B, MXFP4 GEMM
+(fp32 accumulation), i.e. the whole hot path of one GEMM of the triple, with
+the inputs already resident in HBM. The headline workload is the Fprop of a
+Llama-3.1-8B q_proj layer: X 8192x4096 bf16 (0.1% of channels x50), W
+4096x4096 bf16, 32-point Hadamard + RNE along K = 4096, bf16 output.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
+                    [--all] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is TFLOP/s including the two quantizations
+(2*M*N*K / step time). The inputs are replicated so that consecutive steps
+read different copies and the working set exceeds the last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 linear TFLOP/s incl. Hadamard+quant, Llama-3.1-8B shapes; % MFMA peak"
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fprop_q_proj")
+    ap.add_argument("--variant", default=None)
+    ap.add_argument("--all", action="store_true",
+                    help="also time every other workload/variant and the full block")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    return ap.parse_args()
+
+
+class Runner:
+    """Pre-marshalled C-ABI calls for one workload variant (no torch calls in
+    the timed loop)."""
+
+    def __init__(self, mx, w, variant, tensors=None, min_bytes=2 * LLC_BYTES, device="cuda"):
+        import numpy as np
+        import torch
+        from datagen import operands_for, workload_tensors
+
+        self.w = w
+        label, rot, rnd, seed = [v for v in w.variants if v[0] == variant][0]
+        self.variant, self.rot, self.rnd, self.seed = label, rot, rnd, seed
+        t = tensors if tensors is not None else workload_tensors(w)
+        a_src, self.ax_a, b_src, self.ax_b = operands_for(w, t)
+        self.a_shape, self.b_shape = a_src.shape, b_src.shape
+        self.a_src, self.b_src = a_src, b_src
+        per_copy = 2 * (a_src.size + b_src.size)
+        self.ncopy = max(1, math.ceil(min_bytes / per_copy))
+        lib = mx.load_library()
+        self.lib = lib
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(device)
+
+        a0, b0 = dev(a_src), dev(b_src)
+        self.A = [a0] + [a0.clone() for _ in range(self.ncopy - 1)]
+        self.B = [b0] + [b0.clone() for _ in range(self.ncopy - 1)]
+        stream = torch.cuda.current_stream().cuda_stream
+        self.stream = stream
+        seed_a = seed & 0xFFFFFFFF
+        seed_b = seed_a | (1 << 32)
+        self.qa, self.qb, self.qcalls_a, self.qcalls_b = [], [], [], []
+        for i in range(self.ncopy):
+            qa = mx.quantize(self.A[i], self.ax_a, rot, rnd, seed=seed_a)
+            qb = mx.quantize(self.B[i], self.ax_b, rot, rnd, seed=seed_b)
+            self.qa.append(qa)
+            self.qb.append(qb)
+            for q, src, lst in ((qa, self.A[i], self.qcalls_a), (qb, self.B[i], self.qcalls_b)):
+                r, c = src.shape
+                lst.append((src.data_ptr(), r, c, src.stride(0), q.desc.axis, 32,
+                            mx.ROTATE[rot], mx.ROUND[rnd], q.desc.seed, q.codes.data_ptr(),
+                            q.scales.data_ptr(), None, stream))
+        self.M, self.N = self.qa[0].mn, self.qb[0].mn
+        self.K = self.qa[0].k
+        self.out_dtype = w.out_dtype
+        dt = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+        self.C = torch.empty((self.M, self.N), dtype=dt, device=device)
+        self.lcalls = [(mx.OPS[w.op], ctypes.byref(self.qa[i].desc), ctypes.byref(self.qb[i].desc),
+                        self.C.data_ptr(), self.C.stride(0), mx.OUT_DTYPES[w.out_dtype], stream)
+                       for i in range(self.ncopy)]
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        j = i % self.ncopy
+        lib = self.lib
+        if lib.mx_quantize(*self.qcalls_a[j]) or lib.mx_quantize(*self.qcalls_b[j]) or \
+                lib.mx_linear(*self.lcalls[j]):
+            raise RuntimeError("library call failed")
+
+    def quant_a(self, i):
+        if self.lib.mx_quantize(*self.qcalls_a[i % self.ncopy]):
+            raise RuntimeError("mx_quantize failed")
+
+    def quant_b(self, i):
+        if self.lib.mx_quantize(*self.qcalls_b[i % self.ncopy]):
+            raise RuntimeError("mx_quantize failed")
+
+    def gemm(self, i):
+        if self.lib.mx_linear(*self.lcalls[i % self.ncopy]):
+            raise RuntimeError("mx_linear failed")
+
+    # algorithmic work
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def quant_bytes(self, shape):
+        n = shape[0] * shape[1]
+        return n * (2 + 0.5 + 1.0 / 32)
+
+    def gemm_bytes(self):
+        ob = 4 if self.out_dtype == "f32" else 2
+        return (self.M + self.N) * self.K * (0.5 + 1.0 / 32) + self.M * self.N * ob
+
+
+def time_loop(fn, iters, warmup):
+    """Average ms per call of fn(i), HIP events on the current stream (the
+    stream the library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def measure(r, steps, warmup):
+    import torch
+    t_qa = time_loop(r.quant_a, max(steps, 10), 3)
+    t_qb = time_loop(r.quant_b, max(steps, 10), 3)
+    t_g = time_loop(r.gemm, max(steps, 10), 3)
+    for i in range(warmup):
+        r.step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        r.step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    flops = r.flops()
+    return {
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "t_quant_a_us": t_qa * 1e3,
+        "t_quant_b_us": t_qb * 1e3,
+        "t_gemm_us": t_g * 1e3,
+        "gemm_tflops": flops / (t_g * 1e-3) / 1e12,
+        "quant_a_gbs": r.quant_bytes(r.a_shape) / (t_qa * 1e-3) / 1e9,
+        "quant_b_gbs": r.quant_bytes(r.b_shape) / (t_qb * 1e-3) / 1e9,
+    }
+
+
+def cpu_baseline(r, rows):
+    """The oracle on a bounded sample: the first `rows` reduction-major rows of
+    each operand (full K), quantized, then their fp64 GEMM. Per-element
+    quantization time and per-MAC GEMM time are extrapolated to the whole
+    workload and expressed in the metric's unit."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                            if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = None
+    ms = min(rows, r.M)
+    ns = min(rows, r.N)
+
+    def sample(src, axis, n, seed):
+        if axis == 1:
+            return oracle.quantize_ref(src[:n], 1, rotate=r.rot, rounding=r.rnd, seed=seed,
+                                       total_cols=src.shape[1])
+        return oracle.quantize_ref(src[:, :n], 0, rotate=r.rot, rounding=r.rnd, seed=seed,
+                                   col_index=np.arange(n), total_cols=src.shape[1])
+
+    seed_a = r.seed & 0xFFFFFFFF
+    t0 = time.perf_counter()
+    qa = sample(r.a_src, r.ax_a, ms, seed_a)
+    qb = sample(r.b_src, r.ax_b, ns, seed_a | (1 << 32))
+    t1 = time.perf_counter()
+    oracle.mx_gemm_ref(qa, qb)
+    t2 = time.perf_counter()
+    t_elem = (t1 - t0) / ((ms + ns) * r.K)
+    t_mac = (t2 - t1) / (ms * ns * r.K)
+    est = t_elem * (r.M + r.N) * r.K + t_mac * r.M * r.N * r.K
+    return {
+        "value": r.flops() / est / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "quantizer_threads": 1,
+        "kind": "oracle",
+        "sample": (f"oracle quantize of {ms} rows of A and {ns} rows of B (K={r.K}, "
+                   f"{(t1 - t0):.2f} s, NumPy, 1 thread) + fp64 GEMM {ms}x{ns}x{r.K} "
+                   f"({(t2 - t1):.2f} s, BLAS); per-element and per-MAC times "
+                   f"extrapolated to {r.M}x{r.N}x{r.K}"),
+        "sample_seconds": t2 - t0,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+    import torch
+
+    import mxfp4_microscaled_precision_amd as mx
+    from datagen import WORKLOADS, block_workloads, workload_tensors
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    mx.load_library()
+    w = WORKLOADS[args.workload]
+    variant = args.variant or w.variants[0][0]
+    print(f"[bench] workload {w.name} variant {variant}", file=sys.stderr, flush=True)
+    r = Runner(mx, w, variant)
+    res = measure(r, args.steps, args.warmup)
+    t_dom = res["t_gemm_us"]
+    gemm_ach = r.flops() / (t_dom * 1e-6) / 1e12
+    qa_ach = res["quant_a_gbs"]
+    out = {
+        "metric": METRIC,
+        "value": round(res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4_e2m1xfp4_e2m1->f32",
+        "data": "synthetic (seeded PCG64; Llama-3.1-8B q_proj shapes, no real weights)",
+        "config": {
+            "workload": (f"{w.name}: {w.op} M={r.M} N={r.N} K={r.K}, rotate={r.rot}, "
+                         f"round={r.rnd}, out={w.out_dtype}"),
+            "M": r.M, "N": r.N, "K": r.K, "variant": variant, "input_copies": r.ncopy,
+        },
+        "pct_mfma_peak": round(100.0 * res["tflops"] / PEAK_FP4_TFLOPS, 2),
+        "roofline": {
+            "kernel": "mx_gemm (MXFP4 MFMA GEMM)",
+            "bound": "mfma",
+            "achieved": round(gemm_ach, 2),
+            "peak": PEAK_FP4_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_ach / PEAK_FP4_TFLOPS, 4),
+            "traffic": None,
+        },
+        "quant_roofline": {
+            "kernel": f"mx_quant axis {r.ax_a} (operand A)",
+            "bound": "hbm",
+            "achieved": round(qa_ach, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(qa_ach / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "per_kernel_us": {k: round(res[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
+                                                       "t_gemm_us")},
+        "quant_b_gbs": round(res["quant_b_gbs"], 1),
+        "gemm_only_tflops": round(res["gemm_tflops"], 2),
+    }
+    if args.all:
+        extra = {}
+        for name, wl in WORKLOADS.items():
+            if name == "tiny_wgrad":
+                continue
+            t = workload_tensors(wl)
+            for v in wl.variants:
+                if name == w.name and v[0] == variant:
+                    continue
+                rr = Runner(mx, wl, v[0], tensors=t)
+                m = measure(rr, max(10, args.steps // 2), 3)
+                extra[f"{name}/{v[0]}"] = {k: round(val, 3) for k, val in m.items()}
+                print(f"[bench] {name}/{v[0]}: {m['tflops']:.1f} TFLOP/s", file=sys.stderr,
+                      flush=True)
+                del rr
+        out["other_workloads"] = extra
+        out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 5))
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(r, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+def bench_block(mx, wls, steps):
+    """Full Llama-3.1-8B block: 7 linears x {fprop, dgrad, wgrad} per variant."""
+    import torch
+    from datagen import workload_tensors
+    res = {}
+    cache = {}
+    for wl in wls:
+        key = wl.data_seed
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[key] = workload_tensors(wl)
+        for v in wl.variants:
+            rr = Runner(mx, wl, v[0], tensors=cache[key], min_bytes=0)
+            m = measure(rr, steps, 2)
+            d = res.setdefault(v[0], {"flops": 0.0, "ms": 0.0, "ops": {}})
+            d["flops"] += rr.flops()
+            d["ms"] += m["ms_per_step"]
+            d["ops"][wl.name] = {"ms": round(m["ms_per_step"], 4), "tflops": round(m["tflops"], 1),
+                                 "t_gemm_us": round(m["t_gemm_us"], 1)}
+            del rr
+        print(f"[bench] block {wl.name} done", file=sys.stderr, flush=True)
+    for v, d in res.items():
+        d["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 2)
+        d["pct_mfma_peak"] = round(100 * d["tflops"] / PEAK_FP4_TFLOPS, 2)
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 linear-layer library.
+ *
+ * The library computes the three GEMMs of a transformer linear layer with
+ * both operands in MXFP4 (36Kr article "Neue Studie von AMD durchbricht die
+ * bestehende Erkenntnis: Die Instabilitaet von FP4-Training liegt nicht an
+ * unzureichender Zufaelligkeit", section "Fehlerdiagnoseexperiment"):
+ *   Fprop  Y  = X  W^T     X [T, in],  W [out, in]  -> Y  [T, out]
+ *   Dgrad  dX = dY W       dY [T, out], W [out, in] -> dX [T, in]
+ *   Wgrad  dW = dY^T X     dY [T, out], X [T, in]   -> dW [out, in]
+ * Every operand is first rotated along the GEMM reduction axis (none, the
+ * deterministic 32-point Hadamard, or the random-sign Hadamard -- same page,
+ * same section) and then quantized to MXFP4: blocks of 32 elements sharing
+ * one E8M0 exponent, each element an E2M1 4-bit float (same page, section
+ * "Was ist MXFP4?"), rounded to nearest-even or stochastically.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *    on the current HIP device. The caller allocates and owns every buffer;
+ *    the library allocates nothing and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work and return; results are ready when the stream
+ *    reaches them.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is launched and no output byte is written. Nothing throws.
+ *  - Results are bitwise deterministic for identical inputs (no atomics).
+ *  - Calls that write the same buffers concurrently on different streams race.
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (returned by every call). */
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  MX_ERR_SHAPE = -2,       /* bad extents: reduction extent % 32, ld < cols, K mismatch */
+  MX_ERR_ALIGN = -3,       /* a device pointer or leading dimension is misaligned */
+  MX_ERR_ARG = -4,         /* bad enum value, block != 32, axis wrong for the op  */
+  MX_ERR_MISMATCH = -5,    /* A and B were quantized with different rotations / sign seeds */
+  MX_ERR_UNSUPPORTED = -6, /* valid request this build does not implement        */
+  MX_ERR_HIP = -7          /* the HIP runtime reported a launch error            */
+} mx_status;
+
+/* Pre-quantization rotation along the reduction axis (36Kr, section
+ * "Fehlerdiagnoseexperiment": randomized vs deterministic Hadamard). */
+typedef enum mx_rotate {
+  MX_ROT_NONE = 0,
+  MX_ROT_HADAMARD = 1,            /* y = (H32 x) * fp32(1/sqrt 32), H32 Sylvester */
+  MX_ROT_RAND_SIGN_HADAMARD = 2   /* x_k <- s_k x_k first, s_k = +-1 from Philox */
+} mx_rotate;
+
+/* Element rounding (36Kr, "Was ist MXFP4?": nearest; "Fehlerdiagnoseexperiment":
+ * stochastic rounding with zero expected error). */
+typedef enum mx_round {
+  MX_ROUND_RNE = 0,   /* nearest E2M1 value, ties to even mantissa, saturate at 6 */
+  MX_ROUND_SR = 1     /* upper neighbour with probability (a-lo)/(hi-lo), 24-bit uniform */
+} mx_round;
+
+typedef enum mx_op { MX_OP_FPROP = 0, MX_OP_DGRAD = 1, MX_OP_WGRAD = 2 } mx_op;
+
+typedef enum mx_out_dtype { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out_dtype;
+
+/*
+ * A quantized operand, filled by mx_quantize. Its pointers are BORROWED from
+ * the caller (the buffers passed to mx_quantize).
+ *
+ * Packed layout -- always reduction-major ("K-major"), whatever the axis:
+ *   MN = rows, K = cols   when axis == 1 (blocks run along a row);
+ *   MN = cols, K = rows   when axis == 0 (blocks run down a column; the
+ *                         source is written out transposed).
+ *   codes : uint8 [MN][K/2], element (mn, k) in byte k/2, low nibble for
+ *           even k; nibble = sign << 3 | E2M1 magnitude code (0..7 for
+ *           0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   scales: uint8 [MN][K/32], E8M0 code s (value 2^(s-127)); 0xFF marks a
+ *           block that held a NaN or Inf (its codes are 0).
+ * Element value = (-1)^sign * E2M1(mag) * 2^(s - 127).
+ */
+typedef struct mx_qtensor {
+  void *codes;
+  void *scales;
+  int64_t rows, cols;   /* logical bf16 source shape [rows, cols]             */
+  int32_t axis;         /* 0 or 1: the dimension the 32-blocks run along (= K) */
+  int32_t block;        /* always 32                                          */
+  int32_t rotate;       /* mx_rotate used                                     */
+  int32_t round;        /* mx_round used                                      */
+  uint64_t seed;        /* seed used (see mx_quantize)                        */
+} mx_qtensor;
+
+/*
+ * Byte sizes of the packed codes and scales of a [rows, cols] source
+ * quantized along `axis` (see mx_qtensor). Host-only; launches nothing.
+ * Errors: MX_ERR_NULL (null out-pointer), MX_ERR_ARG (axis, block != 32),
+ * MX_ERR_SHAPE (negative extents, or the axis extent not a multiple of 32).
+ */
+mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
+                            size_t *codes_bytes, size_t *scales_bytes);
+
+/*
+ * Rotate + quantize a bf16 tensor into MXFP4 (36Kr, "Was ist MXFP4?": shared
+ * E8M0 exponent per 32-element block from the block maximum, 4-bit elements;
+ * "Fehlerdiagnoseexperiment": Hadamard rotation before quantization).
+ *
+ *  x_bf16  device, bf16 [rows, cols] row-major with leading dimension `ld`
+ *          (elements). Read only.
+ *  axis    1: blocks of 32 along each row (needs cols % 32 == 0);
+ *          0: blocks of 32 down each column (needs rows % 32 == 0).
+ *  block   must be 32.
+ *  rotate  mx_rotate; applied per 32-block along `axis`, before the scale.
+ *  round   mx_round.
+ *  seed    64-bit. Random signs use key (seed_lo, 0) with counter
+ *          (k >> 2, 0, 1, 0), word k & 3, bit 31, for reduction index k, so
+ *          two operands quantized with the same low 32 bits share the signs
+ *          and the rotation cancels in the product. Stochastic rounding uses
+ *          key (seed_lo, seed_hi) with counter (L >> 2 mod 2^32, L >> 34, 0, 0),
+ *          word L & 3, top 24 bits, for the row-major source index
+ *          L = row * cols + col. Generator: Philox4x32-10 (Salmon et al., SC'11).
+ *          Ignored when neither random option is selected.
+ *  codes   device, >= codes_bytes of mx_quantize_sizes, 16-byte aligned. Written.
+ *  scales  device, >= scales_bytes of mx_quantize_sizes. Written.
+ *  out_desc  host, may be NULL; filled with the operand's description.
+ * Requirements: ld >= cols; axis 1: x_bf16 16-byte aligned and ld % 8 == 0;
+ * axis 0: x_bf16 2-byte aligned (any ld; 4-byte-aligned rows load faster).
+ * rows == 0 or cols == 0 is valid and launches nothing.
+ * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_HIP.
+ */
+mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                      int32_t axis, int32_t block, int32_t rotate, int32_t round,
+                      uint64_t seed, void *codes, void *scales, mx_qtensor *out_desc,
+                      void *stream);
+
+/*
+ * One GEMM of the triple over two quantized operands, fp32 accumulation on
+ * the gfx950 block-scaled FP4 matrix cores:
+ *     C[m][n] = sum_k A(m, k) * B(n, k)
+ * with A, B in their K-major packed form (36Kr, "Fehlerdiagnoseexperiment").
+ *
+ *  op = MX_OP_FPROP: A = q(X [T,in], axis 1),  B = q(W [out,in], axis 1); C [T][out]
+ *  op = MX_OP_DGRAD: A = q(dY [T,out], axis 1), B = q(W [out,in], axis 0); C [T][in]
+ *  op = MX_OP_WGRAD: A = q(dY [T,out], axis 0), B = q(X [T,in], axis 0);  C [out][in]
+ *  C        device, row-major [M][N] with leading dimension ldc >= N (elements),
+ *           fp32 or bf16 (round to nearest even of the fp32 accumulator).
+ *           Written; must not overlap A or B.
+ *  stream   hipStream_t as void*.
+ * Both operands must use the same rotation and, for the random-sign rotation,
+ * the same low 32 bits of the seed (else MX_ERR_MISMATCH): that is what makes
+ * the rotation cancel in the product. Their reduction extents must match.
+ * Requirements: C 16-byte aligned for fp32 with ldc % 4 == 0, or 4-byte
+ * aligned for bf16 with ldc % 2 == 0. M, N or K == 0 launches nothing
+ * (K == 0 with M, N > 0 writes zeros).
+ * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN,
+ * MX_ERR_MISMATCH, MX_ERR_HIP.
+ */
+mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C,
+                    int64_t ldc, int32_t out_dtype, void *stream);
+
+/* Static, NUL-terminated name of a status code. Never NULL. */
+const char *mx_status_string(int32_t status);
+
+/* Static, NUL-terminated library version string. */
+const char *mx_version(void);
+
+/* Name of the HIP error behind the most recent MX_ERR_HIP returned to the
+ * calling thread ("hipSuccess" if there was none). Static string; never NULL. */
+const char *mx_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H_ */

@@ -1,0 +1,181 @@
+// C ABI of the MXFP4 library: argument validation and launch dispatch.
+// Every check runs on the host before anything is enqueued, so an invalid
+// call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxfp4.h"
+#include "mx_kernels.h"
+
+namespace {
+
+// HIP error behind the most recent MX_ERR_HIP returned on this thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+mx_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MX_OK;
+  g_last_hip_error = e;
+  return MX_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_rotate(int32_t r) {
+  return r == MX_ROT_NONE || r == MX_ROT_HADAMARD || r == MX_ROT_RAND_SIGN_HADAMARD;
+}
+bool valid_round(int32_t r) { return r == MX_ROUND_RNE || r == MX_ROUND_SR; }
+
+// Reduction (K) and non-reduction (MN) extents of a quantized operand.
+void operand_extents(const mx_qtensor *q, int64_t *mn, int64_t *k) {
+  if (q->axis == 1) {
+    *mn = q->rows;
+    *k = q->cols;
+  } else {
+    *mn = q->cols;
+    *k = q->rows;
+  }
+}
+
+mx_status check_qtensor(const mx_qtensor *q) {
+  if (q == nullptr) return MX_ERR_NULL;
+  if (q->axis != 0 && q->axis != 1) return MX_ERR_ARG;
+  if (q->block != 32) return MX_ERR_ARG;
+  if (!valid_rotate(q->rotate) || !valid_round(q->round)) return MX_ERR_ARG;
+  if (q->rows < 0 || q->cols < 0) return MX_ERR_SHAPE;
+  const int64_t k = q->axis == 1 ? q->cols : q->rows;
+  if (k % 32 != 0) return MX_ERR_SHAPE;
+  if (q->rows > 0 && q->cols > 0) {
+    if (q->codes == nullptr || q->scales == nullptr) return MX_ERR_NULL;
+    if (!aligned(q->codes, 16)) return MX_ERR_ALIGN;
+  }
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
+                            size_t *codes_bytes, size_t *scales_bytes) {
+  if (codes_bytes == nullptr || scales_bytes == nullptr) return MX_ERR_NULL;
+  if (axis != 0 && axis != 1) return MX_ERR_ARG;
+  if (block != 32) return MX_ERR_ARG;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  const int64_t k = axis == 1 ? cols : rows;
+  if (k % 32 != 0) return MX_ERR_SHAPE;
+  *codes_bytes = (size_t)rows * (size_t)cols / 2;
+  *scales_bytes = (size_t)rows * (size_t)cols / 32;
+  return MX_OK;
+}
+
+mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld, int32_t axis,
+                      int32_t block, int32_t rotate, int32_t round, uint64_t seed, void *codes,
+                      void *scales, mx_qtensor *out_desc, void *stream) {
+  if (axis != 0 && axis != 1) return MX_ERR_ARG;
+  if (block != 32) return MX_ERR_ARG;
+  if (!valid_rotate(rotate) || !valid_round(round)) return MX_ERR_ARG;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  const int64_t k = axis == 1 ? cols : rows;
+  if (k % 32 != 0) return MX_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return MX_ERR_NULL;
+    if (ld < cols) return MX_ERR_SHAPE;
+    if (!aligned(codes, 16)) return MX_ERR_ALIGN;
+    if (axis == 1) {
+      if (ld % 8 != 0 || !aligned(x_bf16, 16)) return MX_ERR_ALIGN;
+    } else {
+      if (!aligned(x_bf16, 2)) return MX_ERR_ALIGN;
+    }
+  }
+  if (out_desc != nullptr) {
+    out_desc->codes = codes;
+    out_desc->scales = scales;
+    out_desc->rows = rows;
+    out_desc->cols = cols;
+    out_desc->axis = axis;
+    out_desc->block = block;
+    out_desc->rotate = rotate;
+    out_desc->round = round;
+    out_desc->seed = seed;
+  }
+  if (empty) return MX_OK;
+
+  mx::QuantArgs a;
+  a.x = static_cast<const uint16_t *>(x_bf16);
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.axis = axis;
+  a.rotate = rotate;
+  a.round = round;
+  a.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.codes = static_cast<uint8_t *>(codes);
+  a.scales = static_cast<uint8_t *>(scales);
+  a.rb = 0;
+  return hip_status(mx::quantize_launch(a, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C, int64_t ldc,
+                    int32_t out_dtype, void *stream) {
+  if (op != MX_OP_FPROP && op != MX_OP_DGRAD && op != MX_OP_WGRAD) return MX_ERR_ARG;
+  if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_ARG;
+  mx_status st = check_qtensor(A);
+  if (st != MX_OK) return st;
+  st = check_qtensor(B);
+  if (st != MX_OK) return st;
+  // Which axis each operand must be quantized along, per op.
+  static const int32_t need_axis[3][2] = {{1, 1}, {1, 0}, {0, 0}};
+  if (A->axis != need_axis[op][0] || B->axis != need_axis[op][1]) return MX_ERR_ARG;
+  if (A->rotate != B->rotate) return MX_ERR_MISMATCH;
+  if (A->rotate == MX_ROT_RAND_SIGN_HADAMARD &&
+      (uint32_t)(A->seed & 0xFFFFFFFFull) != (uint32_t)(B->seed & 0xFFFFFFFFull))
+    return MX_ERR_MISMATCH;
+  int64_t M, Ka, N, Kb;
+  operand_extents(A, &M, &Ka);
+  operand_extents(B, &N, &Kb);
+  if (Ka != Kb) return MX_ERR_SHAPE;
+  if (ldc < N) return MX_ERR_SHAPE;
+  if (M == 0 || N == 0) return MX_OK;
+  if (C == nullptr) return MX_ERR_NULL;
+  if (out_dtype == MX_OUT_F32) {
+    if (!aligned(C, 16) || ldc % 4 != 0) return MX_ERR_ALIGN;
+  } else {
+    if (!aligned(C, 4) || ldc % 2 != 0) return MX_ERR_ALIGN;
+  }
+  mx::GemmArgs g;
+  g.a_codes = static_cast<const uint8_t *>(A->codes);
+  g.a_scales = static_cast<const uint8_t *>(A->scales);
+  g.b_codes = static_cast<const uint8_t *>(B->codes);
+  g.b_scales = static_cast<const uint8_t *>(B->scales);
+  g.c = C;
+  g.M = M;
+  g.N = N;
+  g.K = Ka;
+  g.ldc = ldc;
+  g.out_bf16 = out_dtype == MX_OUT_BF16 ? 1 : 0;
+  return hip_status(mx::gemm_launch(g, static_cast<hipStream_t>(stream)));
+}
+
+const char *mx_status_string(int32_t status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: bad extents";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: misaligned pointer or leading dimension";
+    case MX_ERR_ARG: return "MX_ERR_ARG: bad argument value";
+    case MX_ERR_MISMATCH: return "MX_ERR_MISMATCH: operands quantized inconsistently";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED: not implemented";
+    case MX_ERR_HIP: return "MX_ERR_HIP: HIP runtime error";
+    default: return "unknown mx_status";
+  }
+}
+
+const char *mx_version(void) { return "mxfp4-gfx950 0.1.0"; }
+
+const char *mx_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "hipSuccess" : hipGetErrorName(g_last_hip_error);
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Device helpers shared by the gfx950 kernels: Philox4x32-10, bf16 widening,
+// the E8M0 block exponent and the E2M1 element encoders.
+//
+// The MXFP4 format (36Kr article "Neue Studie von AMD durchbricht die
+// bestehende Erkenntnis ...", section "Was ist MXFP4?"): 32-element blocks,
+// one shared E8M0 exponent taken from the largest exponent in the block, and
+// 4-bit elements rounded to the nearest representable value. The element bit
+// split (1 sign, 2 exponent, 1 mantissa) is on the ShowAPI page
+// "AMD颠覆认知：FP4不稳定性的真正原因", section 2.2; exponent bias 1 and the
+// value set {0, 0.5, 1, 1.5, 2, 3, 4, 6} follow OCP MX, the standard the 36Kr
+// page names in "Fazit".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kBlock = 32;
+
+// fp32(1/sqrt(32)): the normalisation that makes the 32-point Sylvester
+// Hadamard orthonormal.
+constexpr uint32_t kInvSqrt32Bits = 0x3E3504F3u;
+
+__device__ __forceinline__ float bits_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f_bits(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): 10 rounds of two 32x32->64 multiplies with the
+// constants below, the key advanced by the two Weyl increments between rounds.
+// ---------------------------------------------------------------------------
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    U4 n;
+    n.x = hi1 ^ c.y ^ k0;
+    n.y = lo1;
+    n.z = hi0 ^ c.w ^ k1;
+    n.w = lo0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+__device__ __forceinline__ uint32_t pick_word(const U4 &v, uint32_t j) {
+  uint32_t r = v.x;
+  r = (j == 1) ? v.y : r;
+  r = (j == 2) ? v.z : r;
+  r = (j == 3) ? v.w : r;
+  return r;
+}
+
+// Random-sign words for reduction indices 4q .. 4q+3 (key (seed_lo, 0),
+// counter (q, 0, 1, 0)); bit 31 of word j is the sign of index 4q + j.
+__device__ __forceinline__ U4 sign_words(uint32_t q, uint32_t seed_lo) {
+  return philox4x32_10(U4{q, 0u, 1u, 0u}, seed_lo, 0u);
+}
+
+// Stochastic-rounding words for source indices 4q .. 4q+3, q = L >> 2 (64-bit):
+// key (seed_lo, seed_hi), counter (q mod 2^32, q >> 32, 0, 0).
+__device__ __forceinline__ U4 sr_words(uint64_t q, uint32_t seed_lo, uint32_t seed_hi) {
+  return philox4x32_10(U4{(uint32_t)q, (uint32_t)(q >> 32), 0u, 0u}, seed_lo, seed_hi);
+}
+
+// ---------------------------------------------------------------------------
+// Block scale. amax_bits = max over the block of (fp32 bits & 0x7fffffff).
+// Returns the unbiased exponent e = clamp(floor(log2 amax) - 2, -127, 127)
+// (-127 for an all-zero block); the caller handles amax_bits >= 0x7f800000
+// (a NaN or Inf in the block) separately.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
+  int E;
+  if (amax_bits >= 0x00800000u) {
+    E = (int)(amax_bits >> 23) - 127;            // normal: biased exponent - 127
+  } else if (amax_bits != 0u) {
+    E = -118 - (int)__clz(amax_bits);            // subnormal: (31 - clz) - 149
+  } else {
+    return -127;
+  }
+  int e = E - 2;                                  // E2M1's largest exponent is 2
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// 2^-e as fp32 for e in [-127, 125] (always a normal number there).
+__device__ __forceinline__ float pow2_neg(int e) {
+  return bits_f((uint32_t)(127 - e) << 23);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 magnitude code of a = |t| (fp32 bits ab, sign cleared), nearest with
+// ties to the even mantissa bit, saturating at 6. Decision thresholds:
+// 0.25 (tie -> 0), 0.75 (tie -> 1.0), 1.25 (tie -> 1.0), 1.75 (tie -> 2),
+// 2.5 (tie -> 2), 3.5 (tie -> 4), 5 (tie -> 4). Integer compares of the
+// non-negative fp32 bit patterns are exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_rne_mag(uint32_t ab) {
+  uint32_t m = 0;
+  m += ab > 0x3E800000u;   // > 0.25
+  m += ab >= 0x3F400000u;  // >= 0.75
+  m += ab > 0x3FA00000u;   // > 1.25
+  m += ab >= 0x3FE00000u;  // >= 1.75
+  m += ab > 0x40200000u;   // > 2.5
+  m += ab >= 0x40600000u;  // >= 3.5
+  m += ab > 0x40A00000u;   // > 5.0
+  return m;
+}
+
+// Stochastic E2M1 magnitude code: lo <= a < hi neighbours, upper one taken
+// when u24 < f * 2^24 with f = (a - lo) / (hi - lo). Both a - lo (Sterbenz)
+// and the division by the power-of-two gap are exact in fp32, as is the
+// comparison with the integer u24 < 2^24. a >= 6 gives 6 (not randomised).
+__device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
+  uint32_t idx = 0;
+  idx += ab >= 0x3F000000u;  // 0.5
+  idx += ab >= 0x3F800000u;  // 1
+  idx += ab >= 0x3FC00000u;  // 1.5
+  idx += ab >= 0x40000000u;  // 2
+  idx += ab >= 0x40400000u;  // 3
+  idx += ab >= 0x40800000u;  // 4
+  idx += ab >= 0x40C00000u;  // 6
+  if (idx >= 7) return 7;
+  // lo and 2^24 / gap for each lower-neighbour index
+  float lo, inv_gap24;
+  switch (idx) {
+    case 0: lo = 0.0f; inv_gap24 = 33554432.0f; break;  // gap 0.5
+    case 1: lo = 0.5f; inv_gap24 = 33554432.0f; break;
+    case 2: lo = 1.0f; inv_gap24 = 33554432.0f; break;
+    case 3: lo = 1.5f; inv_gap24 = 33554432.0f; break;
+    case 4: lo = 2.0f; inv_gap24 = 16777216.0f; break;  // gap 1
+    case 5: lo = 3.0f; inv_gap24 = 16777216.0f; break;
+    default: lo = 4.0f; inv_gap24 = 8388608.0f; break;  // gap 2
+  }
+  const float a = bits_f(ab);
+  const float thr = __fmul_rn(__fsub_rn(a, lo), inv_gap24);
+  return idx + ((float)u24 < thr ? 1u : 0u);
+}
+
+}  // namespace mx

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (mx_api.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace mx {
+
+// Launch `kernel` and return that launch's own status (never a sticky error
+// left behind by an unrelated earlier HIP call). Arguments are converted to
+// the kernel's exact parameter types before their addresses are taken.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> params{static_cast<KArgs>(args)...};
+  void *ptrs[sizeof...(KArgs)];
+  std::apply([&](auto &...p) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void *>(&p)), ...);
+  }, params);
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shmem, stream);
+}
+
+enum { MX_K_ROT_NONE = 0, MX_K_ROT_HADAMARD = 1, MX_K_ROT_RAND_SIGN = 2 };
+enum { MX_K_ROUND_RNE = 0, MX_K_ROUND_SR = 1 };
+
+struct QuantArgs {
+  const uint16_t *x;   // bf16 [rows, cols], leading dimension ld
+  int64_t rows, cols, ld;
+  int axis;            // 0 or 1
+  int rotate, round;
+  uint32_t seed_lo, seed_hi;
+  uint8_t *codes;      // K-major packed codes
+  uint8_t *scales;     // K-major scales
+  int rb;              // axis-0 row blocks per lane (0 = default)
+};
+
+hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t *a_codes, *a_scales;  // [M][K/2], [M][K/32]
+  const uint8_t *b_codes, *b_scales;  // [N][K/2], [N][K/32]
+  void *c;                            // [M][N], leading dimension ldc
+  int64_t M, N, K, ldc;
+  int out_bf16;
+};
+
+hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: every declared symbol is exported, and every
+invalid argument is rejected on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (the library must bind to torch's HIP runtime)
+
+import mxfp4_microscaled_precision_amd as mx
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mxfp4.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(mx.library_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mx.LIB_PATH)
+    assert len(mx._hip_runtimes_mapped()) <= 1
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert mx.version().startswith("mxfp4-gfx950")
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert mx.status_string(s).startswith("MX_")
+    assert mx.last_hip_error() == "hipSuccess"
+    assert "unknown" in mx.status_string(42)
+
+
+def test_quantize_sizes():
+    assert mx.quantize_sizes(8192, 4096, 1) == (8192 * 4096 // 2, 8192 * 4096 // 32)
+    assert mx.quantize_sizes(256, 96, 0) == (256 * 96 // 2, 256 * 96 // 32)
+    assert mx.quantize_sizes(0, 0, 1) == (0, 0)
+    for args, code in [((64, 48, 1), -2), ((48, 64, 0), -2), ((64, 64, 2), -4),
+                       ((-1, 64, 1), -2)]:
+        with pytest.raises(mx.MxError) as ei:
+            mx.quantize_sizes(*args)
+        assert ei.value.status == code
+    with pytest.raises(mx.MxError) as ei:
+        mx.quantize_sizes(64, 64, 1, block=16)
+    assert ei.value.status == -4
+
+
+def _q(lib, x, rows, cols, ld, axis=1, block=32, rot=1, rnd=0, codes=16, scales=16):
+    desc = mx.QTensorDesc()
+    return lib.mx_quantize(x, rows, cols, ld, axis, block, rot, rnd, 0, codes, scales,
+                           ctypes.byref(desc), None)
+
+
+def test_quantize_rejects_before_launch():
+    """Host pointers are never dereferenced: validation fails before any HIP call."""
+    lib = mx.load_library()
+    P = 4096  # a fake, 16-byte-aligned address; never touched
+    assert _q(lib, P, 64, 64, 64, block=16) == -4
+    assert _q(lib, P, 64, 64, 64, axis=2) == -4
+    assert _q(lib, P, 64, 64, 64, rot=3) == -4
+    assert _q(lib, P, 64, 64, 64, rnd=2) == -4
+    assert _q(lib, P, 64, 48, 64, axis=1) == -2          # cols % 32
+    assert _q(lib, P, 48, 64, 64, axis=0) == -2          # rows % 32
+    assert _q(lib, P, 64, 64, 32) == -2                  # ld < cols
+    assert _q(lib, P, 64, 64, 68) == -3                  # ld % 8 (axis 1)
+    assert _q(lib, P + 2, 64, 64, 64) == -3              # x misaligned (axis 1)
+    assert _q(lib, P + 1, 64, 64, 64, axis=0) == -3      # x odd address (axis 0)
+    assert _q(lib, P, 64, 64, 64, codes=P + 4) == -3     # codes misaligned
+    assert _q(lib, None, 64, 64, 64) == -1
+    assert _q(lib, P, 64, 64, 64, codes=None) == -1
+    assert _q(lib, P, 64, 64, 64, scales=None) == -1
+    assert _q(lib, P, -1, 64, 64) == -2
+
+
+def test_quantize_empty_is_a_noop_and_fills_descriptor():
+    lib = mx.load_library()
+    desc = mx.QTensorDesc()
+    assert lib.mx_quantize(None, 0, 64, 64, 1, 32, 2, 1, 77, None, None, ctypes.byref(desc),
+                           None) == 0
+    assert (desc.rows, desc.cols, desc.axis, desc.rotate, desc.round, desc.seed) == (0, 64, 1, 2, 1, 77)
+
+
+def _desc(rows, cols, axis, rot=1, rnd=0, seed=0, codes=4096, scales=4096):
+    d = mx.QTensorDesc()
+    d.codes, d.scales = codes, scales
+    d.rows, d.cols, d.axis, d.block, d.rotate, d.round, d.seed = rows, cols, axis, 32, rot, rnd, seed
+    return d
+
+
+def _lin(lib, op, A, B, C=4096, ldc=None, out=0):
+    ldc = ldc if ldc is not None else (B.rows if B.axis == 1 else B.cols)
+    return lib.mx_linear(op, ctypes.byref(A), ctypes.byref(B), C, ldc, out, None)
+
+
+def test_linear_rejects_before_launch():
+    lib = mx.load_library()
+    X, W = _desc(64, 128, 1), _desc(96, 128, 1)
+    assert _lin(lib, 3, X, W) == -4                       # bad op
+    assert _lin(lib, 0, X, W, out=2) == -4                # bad dtype
+    assert _lin(lib, 1, X, W) == -4                       # dgrad needs B on axis 0
+    assert _lin(lib, 2, X, W) == -4                       # wgrad needs axis 0 for both
+    assert _lin(lib, 0, X, _desc(96, 160, 1)) == -2       # K mismatch
+    assert _lin(lib, 0, X, _desc(96, 128, 1, rot=0)) == -5
+    assert _lin(lib, 0, _desc(64, 128, 1, rot=2, seed=1), _desc(96, 128, 1, rot=2, seed=2)) == -5
+    # same low 32 bits, different role in the high bits: accepted by validation
+    # (so pass a NULL C to stop at the pointer check instead of launching)
+    assert _lin(lib, 0, _desc(64, 128, 1, rot=2, seed=1), _desc(96, 128, 1, rot=2, seed=1 | 1 << 32),
+                C=None) == -1
+    assert _lin(lib, 0, X, W, ldc=95) == -2               # ldc < N
+    assert _lin(lib, 0, X, W, C=4096 + 4) == -3           # fp32 C misaligned
+    assert _lin(lib, 0, X, W, ldc=98) == -3               # fp32 ldc % 4
+    assert _lin(lib, 0, X, W, C=4096 + 2, out=1) == -3    # bf16 C misaligned
+    assert _lin(lib, 0, X, W, C=None) == -1
+    assert _lin(lib, 0, _desc(64, 128, 1, codes=None), W) == -1
+    assert _lin(lib, 0, _desc(64, 128, 1, codes=4100), W) == -3
+    bad = _desc(64, 128, 1)
+    bad.block = 16
+    assert _lin(lib, 0, bad, W) == -4
+    assert lib.mx_linear(0, None, ctypes.byref(W), 4096, 96, 0, None) == -1
+
+
+def test_linear_empty_is_a_noop():
+    lib = mx.load_library()
+    assert _lin(lib, 0, _desc(0, 128, 1), _desc(96, 128, 1), C=None) == 0
+    assert _lin(lib, 2, _desc(64, 0, 0), _desc(64, 32, 0), C=None) == 0

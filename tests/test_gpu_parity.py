@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bar: E2M1 codes and E8M0 scales bit-exact (stochastic rounding included, for
+a given seed); GEMM outputs within 1e-5 relative Frobenius error of the fp64
+oracle GEMM over the dequantized operands; bf16 outputs equal to the
+round-to-nearest-even of the same GEMM's fp32 output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from datagen import (WORKLOADS, f32_to_bf16_bits, operands_for, workload_tensors)
+from gpu_util import host_u8, rel_fro, to_dev, to_dev_strided
+
+pytestmark = pytest.mark.gpu
+
+ROTS = ("none", "hadamard", "rand_sign_hadamard")
+RNDS = ("rne", "sr")
+GEMM_TOL = 1e-5
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _check_q(q_gpu, ref, what=""):
+    codes = host_u8(q_gpu.codes)
+    scales = host_u8(q_gpu.scales)
+    want_codes = oracle.pack_codes(ref.codes)
+    assert codes.shape == want_codes.shape, what
+    bad = np.count_nonzero(codes != want_codes)
+    bad_s = np.count_nonzero(scales != ref.scales)
+    assert bad == 0 and bad_s == 0, f"{what}: {bad} code bytes, {bad_s} scales differ"
+
+
+def _rand_bits(rng, shape, scale=1.0):
+    return f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+# ------------------------------------------------------------------ quantizer
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_small_ragged(mx, axis, rot, rnd):
+    rng = np.random.default_rng(100 + axis)
+    shape = (37, 160) if axis == 1 else (160, 37)      # ragged non-axis extent
+    x = _rand_bits(rng, shape)
+    seed = 0x1234 | (1 << 32)
+    q = mx.quantize(to_dev(x), axis=axis, rotate=rot, round=rnd, seed=seed)
+    _sync()
+    ref = oracle.quantize_ref(x, axis, rotate=rot, rounding=rnd, seed=seed)
+    _check_q(q, ref, f"axis={axis} rot={rot} rnd={rnd}")
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+def test_quantize_strided_input(mx, axis):
+    rng = np.random.default_rng(7)
+    shape = (64, 96) if axis == 1 else (96, 66)
+    x = _rand_bits(rng, shape, 3.0)
+    t = to_dev_strided(x, ld=shape[1] + 30 + (8 - (shape[1] + 30) % 8) % 8)
+    q = mx.quantize(t, axis=axis, rotate="rand_sign_hadamard", round="sr", seed=99)
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, axis, rotate="rand_sign_hadamard", rounding="sr", seed=99))
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+@pytest.mark.parametrize("rot", ("none", "hadamard"))
+def test_quantize_every_bf16_pattern(mx, axis, rot):
+    """All 65536 bf16 bit patterns (NaN/Inf/subnormal included), plus every
+    pattern again with a 7.97 anchor leading each block."""
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    blocks = allv.reshape(2048, 32)
+    n_anch = -(-65536 // 31)
+    pad = np.zeros(n_anch * 31, np.uint16)
+    pad[:65536] = allv
+    anch = np.concatenate([np.full((n_anch, 1), 0x40FF, np.uint16), pad.reshape(n_anch, 31)], 1)
+    x = np.concatenate([blocks, anch], 0)
+    if axis == 0:
+        x = np.ascontiguousarray(x.T)
+    q = mx.quantize(to_dev(x), axis=axis, rotate=rot, round="rne")
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, axis, rotate=rot), f"axis={axis} rot={rot}")
+
+
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_special_blocks(mx, rot, rnd):
+    f = np.float32
+    rows = [
+        np.zeros(32, f), np.full(32, -0.0, f), np.ones(32, f),
+        np.eye(32, dtype=f)[3], np.full(32, 3.0e38, f),            # overflow inside the butterfly
+        np.where(np.arange(32) % 2 == 0, 3.0e38, -3.0e38).astype(f),
+        np.full(32, 1e-40, f), np.linspace(-1e-39, 1e-39, 32).astype(f),
+        np.r_[np.full(31, 1.0, f), f(np.inf)], np.r_[np.full(31, 1.0, f), f(-np.inf)],
+        np.r_[np.full(31, 1.0, f), f(np.nan)], np.r_[np.full(16, f(np.inf)), np.full(16, -np.inf)].astype(f),
+        np.full(32, 5.0, f), np.full(32, 2.5, f), np.full(32, 0.75, f),
+        np.linspace(-6, 6, 32).astype(f), np.ldexp(np.ones(32, f), np.arange(-16, 16)).astype(f),
+    ]
+    x = f32_to_bf16_bits(np.stack(rows))
+    x = np.concatenate([x, x[::-1]], 1)                    # 64 columns
+    for axis in (1, 0):
+        xa = x if axis == 1 else np.ascontiguousarray(x.T)
+        q = mx.quantize(to_dev(xa), axis=axis, rotate=rot, round=rnd, seed=3)
+        _sync()
+        _check_q(q, oracle.quantize_ref(xa, axis, rotate=rot, rounding=rnd, seed=3),
+                 f"axis={axis} rot={rot} rnd={rnd}")
+
+
+def test_quantize_determinism_and_seed_use(mx):
+    rng = np.random.default_rng(11)
+    x = to_dev(_rand_bits(rng, (128, 256)))
+    a = mx.quantize(x, 1, "hadamard", "rne", seed=1)
+    b = mx.quantize(x, 1, "hadamard", "rne", seed=2)            # seed unused
+    c = mx.quantize(x, 1, "none", "sr", seed=5)
+    d = mx.quantize(x, 1, "none", "sr", seed=5)
+    e = mx.quantize(x, 1, "none", "sr", seed=6)
+    _sync()
+    assert np.array_equal(host_u8(a.codes), host_u8(b.codes))
+    assert np.array_equal(host_u8(c.codes), host_u8(d.codes))
+    assert not np.array_equal(host_u8(c.codes), host_u8(e.codes))
+
+
+def test_quantize_empty(mx):
+    import torch
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q = mx.quantize(x, 1)
+    assert q.codes.numel() == 0 and q.scales.numel() == 0
+
+
+# ----------------------------------------------------------------------- GEMM
+def _gemm_case(mx, op, a_src, b_src, rot, rnd, seed, check_bf16=True):
+    ax_a, ax_b = mx.OP_AXES[op]
+    qa = mx.quantize(to_dev(a_src), ax_a, rot, rnd, seed=seed & 0xFFFFFFFF)
+    qb = mx.quantize(to_dev(b_src), ax_b, rot, rnd, seed=(seed & 0xFFFFFFFF) | (1 << 32))
+    c32 = mx.linear(op, qa, qb, "f32")
+    c16 = mx.linear(op, qa, qb, "bf16") if check_bf16 else None
+    _sync()
+    C_ref, ra, rb = oracle.linear_ref(op, a_src, b_src, rotate=rot, rounding=rnd, seed=seed)
+    _check_q(qa, ra, f"{op} A")
+    _check_q(qb, rb, f"{op} B")
+    got = c32.cpu().numpy()
+    err = rel_fro(got, C_ref)
+    assert err <= GEMM_TOL, f"{op} {rot} {rnd}: rel Frobenius {err:.3e}"
+    if check_bf16:
+        import torch
+        b16 = c16.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(b16, oracle.bf16_round_ref(got)), "bf16 epilogue != RNE(fp32)"
+    return err
+
+
+def test_gemm_tiny_wgrad_workload(mx):
+    """dY 256x128 and X 256x96, N(0,1), seed 0; H32 + RNE along the 256 tokens;
+    dW = dY^T X, 128x96 fp32."""
+    w = WORKLOADS["tiny_wgrad"]
+    t = workload_tensors(w)
+    a, _, b, _ = operands_for(w, t)
+    _gemm_case(mx, "wgrad", a, b, "hadamard", "rne", 0)
+
+
+@pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("rot,rnd", [("hadamard", "rne"), ("rand_sign_hadamard", "rne"),
+                                     ("none", "sr"), ("none", "rne")])
+def test_gemm_ops_ragged(mx, op, rot, rnd):
+    """T=224, out=96, in=160: every op has M, N off the 128 tile and a K tail."""
+    rng = np.random.default_rng(21)
+    T, o, i = 224, 96, 160
+    X = _rand_bits(rng, (T, i))
+    W = _rand_bits(rng, (o, i), 0.02)
+    dY = f32_to_bf16_bits((rng.standard_t(3, (T, o)) * 1e-4).astype(np.float32))
+    a, b = {"fprop": (X, W), "dgrad": (dY, W), "wgrad": (dY, X)}[op]
+    _gemm_case(mx, op, a, b, rot, rnd, 11)
+
+
+def test_gemm_several_tiles(mx):
+    rng = np.random.default_rng(22)
+    A = _rand_bits(rng, (640, 1024))
+    B = _rand_bits(rng, (392, 1024))
+    _gemm_case(mx, "fprop", A, B, "hadamard", "rne", 0)
+
+
+def test_gemm_k_zero_writes_zeros(mx):
+    import torch
+    A = mx.quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), 0)
+    B = mx.quantize(torch.empty((0, 48), dtype=torch.bfloat16, device="cuda"), 0)
+    out = torch.full((64, 48), float("nan"), device="cuda")
+    mx.linear("wgrad", A, B, "f32", out=out)
+    _sync()
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_gemm_deterministic(mx):
+    rng = np.random.default_rng(23)
+    qa = mx.quantize(to_dev(_rand_bits(rng, (512, 2048))), 1)
+    qb = mx.quantize(to_dev(_rand_bits(rng, (384, 2048))), 1)
+    c1 = mx.linear("fprop", qa, qb)
+    c2 = mx.linear("fprop", qa, qb)
+    _sync()
+    assert np.array_equal(c1.cpu().numpy().view(np.uint32), c2.cpu().numpy().view(np.uint32))
+
+
+# --------------------------------------------- full-size workloads, sampled
+FULL = [("fprop_q_proj", "det_hadamard"), ("wgrad_gate_proj", "no_rotation"),
+        ("wgrad_gate_proj", "det_hadamard"), ("dgrad_down_proj", "det_hadamard"),
+        ("dgrad_down_proj", "det_hadamard_sr7")]
+
+
+@pytest.mark.parametrize("name,variant", FULL)
+def test_full_size_sampled(mx, name, variant):
+    """Full workload sizes in the launch configuration the bench times;
+    sampled operand rows are checked bit for bit and the sampled output
+    block C[ms, ns] against the oracle."""
+    w = WORKLOADS[name]
+    _, rot, rnd, seed = [v for v in w.variants if v[0] == variant][0]
+    t = workload_tensors(w)
+    a_src, ax_a, b_src, ax_b = operands_for(w, t)
+    seed_a, seed_b = seed & 0xFFFFFFFF, (seed & 0xFFFFFFFF) | (1 << 32)
+    qa = mx.quantize(to_dev(a_src), ax_a, rot, rnd, seed=seed_a)
+    qb = mx.quantize(to_dev(b_src), ax_b, rot, rnd, seed=seed_b)
+    c = mx.linear(w.op, qa, qb, "f32")
+    _sync()
+    rng = np.random.default_rng(5)
+    M, N = qa.mn, qb.mn
+    ms = np.sort(rng.choice(M, 48, replace=False))
+    ns = np.sort(rng.choice(N, 48, replace=False))
+
+    def ref_rows(src, axis, idx, s):
+        if axis == 1:
+            return oracle.quantize_ref(src[idx], 1, rotate=rot, rounding=rnd, seed=s,
+                                       row_index=idx, total_cols=src.shape[1])
+        return oracle.quantize_ref(src[:, idx], 0, rotate=rot, rounding=rnd, seed=s,
+                                   col_index=idx, total_cols=src.shape[1])
+
+    ra = ref_rows(a_src, ax_a, ms, seed_a)
+    rb = ref_rows(b_src, ax_b, ns, seed_b)
+    assert np.array_equal(host_u8(qa.codes[ms]), oracle.pack_codes(ra.codes))
+    assert np.array_equal(host_u8(qa.scales[ms]), ra.scales)
+    assert np.array_equal(host_u8(qb.codes[ns]), oracle.pack_codes(rb.codes))
+    assert np.array_equal(host_u8(qb.scales[ns]), rb.scales)
+    C_ref = oracle.mx_gemm_ref(ra, rb)
+    got = c.cpu().numpy()[np.ix_(ms, ns)]
+    err = rel_fro(got, C_ref)
+    assert err <= GEMM_TOL, f"{name}/{variant}: rel Frobenius {err:.3e}"
