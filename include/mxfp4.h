@@ -151,9 +151,8 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
  * Both operands must use the same rotation and, for the random-sign rotation,
  * the same low 32 bits of the seed (else MX_ERR_MISMATCH): that is what makes
  * the rotation cancel in the product. Their reduction extents must match.
- * Requirements: C 16-byte aligned for fp32 with ldc % 4 == 0, or 4-byte
- * aligned for bf16 with ldc % 2 == 0. M, N or K == 0 launches nothing
- * (K == 0 with M, N > 0 writes zeros).
+ * Requirements: C aligned to its element size (4 bytes for fp32, 2 for bf16),
+ * ldc >= N. M or N == 0 launches nothing; K == 0 with M, N > 0 writes zeros.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN,
  * MX_ERR_MISMATCH, MX_ERR_HIP.
  */

@@ -139,11 +139,7 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
   if (ldc < N) return MX_ERR_SHAPE;
   if (M == 0 || N == 0) return MX_OK;
   if (C == nullptr) return MX_ERR_NULL;
-  if (out_dtype == MX_OUT_F32) {
-    if (!aligned(C, 16) || ldc % 4 != 0) return MX_ERR_ALIGN;
-  } else {
-    if (!aligned(C, 4) || ldc % 2 != 0) return MX_ERR_ALIGN;
-  }
+  if (!aligned(C, out_dtype == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
   mx::GemmArgs g;
   g.a_codes = static_cast<const uint8_t *>(A->codes);
   g.a_scales = static_cast<const uint8_t *>(A->scales);

@@ -113,9 +113,8 @@ def test_linear_rejects_before_launch():
     assert _lin(lib, 0, _desc(64, 128, 1, rot=2, seed=1), _desc(96, 128, 1, rot=2, seed=1 | 1 << 32),
                 C=None) == -1
     assert _lin(lib, 0, X, W, ldc=95) == -2               # ldc < N
-    assert _lin(lib, 0, X, W, C=4096 + 4) == -3           # fp32 C misaligned
-    assert _lin(lib, 0, X, W, ldc=98) == -3               # fp32 ldc % 4
-    assert _lin(lib, 0, X, W, C=4096 + 2, out=1) == -3    # bf16 C misaligned
+    assert _lin(lib, 0, X, W, C=4096 + 2) == -3           # fp32 C not 4-byte aligned
+    assert _lin(lib, 0, X, W, C=4096 + 1, out=1) == -3    # bf16 C not 2-byte aligned
     assert _lin(lib, 0, X, W, C=None) == -1
     assert _lin(lib, 0, _desc(64, 128, 1, codes=None), W) == -1
     assert _lin(lib, 0, _desc(64, 128, 1, codes=4100), W) == -3

@@ -172,6 +172,17 @@ def test_gemm_ops_ragged(mx, op, rot, rnd):
     _gemm_case(mx, op, a, b, rot, rnd, 11)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 200, 384), (520, 260, 640), (256, 256, 128),
+                                   (1, 1, 128), (257, 513, 1152)])
+def test_gemm_lds_path_tails(mx, M, N, K):
+    """K % 128 == 0 (the LDS-staged kernel) with ragged M / N and a half-stage
+    K tail (K % 256 == 128)."""
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A = _rand_bits(rng, (M, K))
+    B = _rand_bits(rng, (N, K), 0.5)
+    _gemm_case(mx, "fprop", A, B, "hadamard", "rne", 0)
+
+
 def test_gemm_several_tiles(mx):
     rng = np.random.default_rng(22)
     A = _rand_bits(rng, (640, 1024))
