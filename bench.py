@@ -45,6 +45,9 @@ def parse():
                     help="also time every other workload/variant and the full block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB three "
+                         "times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -313,6 +316,14 @@ def main():
                 del rr
         out["other_workloads"] = extra
         out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 5))
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(r, args.cpu_sample_rows)

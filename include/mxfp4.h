@@ -71,15 +71,24 @@ typedef enum mx_out_dtype { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out_dtype;
  * A quantized operand, filled by mx_quantize. Its pointers are BORROWED from
  * the caller (the buffers passed to mx_quantize).
  *
- * Packed layout -- always reduction-major ("K-major"), whatever the axis:
+ * The operand is always stored reduction-major ("K-major"), whatever the axis:
  *   MN = rows, K = cols   when axis == 1 (blocks run along a row);
  *   MN = cols, K = rows   when axis == 0 (blocks run down a column; the
  *                         source is written out transposed).
- *   codes : uint8 [MN][K/2], element (mn, k) in byte k/2, low nibble for
- *           even k; nibble = sign << 3 | E2M1 magnitude code (0..7 for
+ * It is zero-padded to MNp = MN rounded up to 16 and Kp = K rounded up to
+ * 128, and stored in 16 x 128 tiles, the fragment shape of the gfx950 FP4
+ * matrix instruction, so the GEMM streams every tile as one contiguous 1 KB:
+ *   codes : MNp * Kp / 2 bytes. Tile (g, q) -- rows 16g..16g+15, K elements
+ *           128q..128q+127 -- is the 1 KB at byte (g * Kp/128 + q) * 1024;
+ *           inside it, 32-element block c (0..3) of row r (0..15) is the 16
+ *           bytes at c * 256 + r * 16, two codes per byte, the even K index in
+ *           the low nibble. Code = sign << 3 | E2M1 magnitude code (0..7 for
  *           0, 0.5, 1, 1.5, 2, 3, 4, 6).
- *   scales: uint8 [MN][K/32], E8M0 code s (value 2^(s-127)); 0xFF marks a
- *           block that held a NaN or Inf (its codes are 0).
+ *   scales: MNp * Kp / 32 bytes, [Kp/128][MNp][4]: the E8M0 code s (value
+ *           2^(s-127)) of block kb of row mn is at byte
+ *           ((kb / 4) * MNp + mn) * 4 + kb % 4. 0xFF marks a block that held a
+ *           NaN or Inf (its codes are 0).
+ * Padding rows and blocks hold the encoding of zeros (codes 0, scale code 0).
  * Element value = (-1)^sign * E2M1(mag) * 2^(s - 127).
  */
 typedef struct mx_qtensor {
@@ -94,8 +103,8 @@ typedef struct mx_qtensor {
 } mx_qtensor;
 
 /*
- * Byte sizes of the packed codes and scales of a [rows, cols] source
- * quantized along `axis` (see mx_qtensor). Host-only; launches nothing.
+ * Byte sizes of the tiled codes and scales of a [rows, cols] source quantized
+ * along `axis`, padding included (see mx_qtensor). Host-only; launches nothing.
  * Errors: MX_ERR_NULL (null out-pointer), MX_ERR_ARG (axis, block != 32),
  * MX_ERR_SHAPE (negative extents, or the axis extent not a multiple of 32).
  */
@@ -122,13 +131,18 @@ mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t bl
  *          word L & 3, top 24 bits, for the row-major source index
  *          L = row * cols + col. Generator: Philox4x32-10 (Salmon et al., SC'11).
  *          Ignored when neither random option is selected.
- *  codes   device, >= codes_bytes of mx_quantize_sizes, 16-byte aligned. Written.
- *  scales  device, >= scales_bytes of mx_quantize_sizes. Written.
+ *  codes   device, >= codes_bytes of mx_quantize_sizes, 16-byte aligned. Written
+ *          in full (padding included).
+ *  scales  device, >= scales_bytes of mx_quantize_sizes, 4-byte aligned. Written
+ *          in full.
  *  out_desc  host, may be NULL; filled with the operand's description.
  * Requirements: ld >= cols; axis 1: x_bf16 16-byte aligned and ld % 8 == 0;
  * axis 0: x_bf16 2-byte aligned (any ld; 4-byte-aligned rows load faster).
  * rows == 0 or cols == 0 is valid and launches nothing.
- * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_HIP.
+ * Limit: the padded codes (MNp * Kp / 2 bytes) must stay below 1 GiB, else
+ * MX_ERR_UNSUPPORTED.
+ * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_UNSUPPORTED,
+ * MX_ERR_HIP.
  */
 mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
                       int32_t axis, int32_t block, int32_t rotate, int32_t round,
@@ -139,7 +153,7 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
  * One GEMM of the triple over two quantized operands, fp32 accumulation on
  * the gfx950 block-scaled FP4 matrix cores:
  *     C[m][n] = sum_k A(m, k) * B(n, k)
- * with A, B in their K-major packed form (36Kr, "Fehlerdiagnoseexperiment").
+ * with A, B in their tiled K-major form (36Kr, "Fehlerdiagnoseexperiment").
  *
  *  op = MX_OP_FPROP: A = q(X [T,in], axis 1),  B = q(W [out,in], axis 1); C [T][out]
  *  op = MX_OP_DGRAD: A = q(dY [T,out], axis 1), B = q(W [out,in], axis 0); C [T][in]

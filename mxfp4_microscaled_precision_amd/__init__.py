@@ -158,8 +158,9 @@ def _stream_handle(device, stream) -> int:
 
 
 class QTensor:
-    """A quantized operand: packed codes [MN, K/2] and scales [MN, K/32] (uint8,
-    reduction-major) plus the C descriptor that points at them."""
+    """A quantized operand: flat uint8 buffers holding the tiled codes and
+    scales (layout in include/mxfp4.h, struct mx_qtensor) plus the C
+    descriptor that points at them."""
 
     def __init__(self, codes, scales, desc: QTensorDesc):
         self.codes = codes
@@ -201,11 +202,10 @@ def quantize(x, axis: int, rotate: str = "hadamard", round: str = "rne", seed: i
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else max(cols, 8 * ((cols + 7) // 8))
     cb, sb = quantize_sizes(rows, cols, axis)
-    mn, k = (rows, cols) if axis == 1 else (cols, rows)
     if codes is None:
-        codes = torch.empty((mn, k // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((cb,), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((mn, k // 32), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((sb,), dtype=torch.uint8, device=x.device)
     if codes.numel() < cb or scales.numel() < sb:
         raise ValueError("codes / scales buffers too small")
     desc = QTensorDesc()

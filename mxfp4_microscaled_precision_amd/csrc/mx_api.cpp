@@ -36,6 +36,20 @@ void operand_extents(const mx_qtensor *q, int64_t *mn, int64_t *k) {
   }
 }
 
+// Tiled-layout extents: MN up to a multiple of 16, K up to a multiple of 128
+// (empty operands stay empty).
+void padded_extents(int64_t rows, int64_t cols, int32_t axis, int64_t *mnp, int64_t *kp) {
+  const int64_t mn = axis == 1 ? rows : cols;
+  const int64_t k = axis == 1 ? cols : rows;
+  const bool empty = rows == 0 || cols == 0;
+  *mnp = empty ? 0 : (mn + 15) / 16 * 16;
+  *kp = empty ? 0 : (k + 127) / 128 * 128;
+}
+
+// The GEMM addresses each operand's codes with 32-bit signed offsets (one
+// 256-row block tile past the end must still be representable).
+constexpr int64_t kMaxCodeBytes = (int64_t)1 << 30;
+
 mx_status check_qtensor(const mx_qtensor *q) {
   if (q == nullptr) return MX_ERR_NULL;
   if (q->axis != 0 && q->axis != 1) return MX_ERR_ARG;
@@ -46,7 +60,10 @@ mx_status check_qtensor(const mx_qtensor *q) {
   if (k % 32 != 0) return MX_ERR_SHAPE;
   if (q->rows > 0 && q->cols > 0) {
     if (q->codes == nullptr || q->scales == nullptr) return MX_ERR_NULL;
-    if (!aligned(q->codes, 16)) return MX_ERR_ALIGN;
+    if (!aligned(q->codes, 16) || !aligned(q->scales, 4)) return MX_ERR_ALIGN;
+    int64_t mnp, kp;
+    padded_extents(q->rows, q->cols, q->axis, &mnp, &kp);
+    if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
   }
   return MX_OK;
 }
@@ -63,8 +80,10 @@ mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t bl
   if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
   const int64_t k = axis == 1 ? cols : rows;
   if (k % 32 != 0) return MX_ERR_SHAPE;
-  *codes_bytes = (size_t)rows * (size_t)cols / 2;
-  *scales_bytes = (size_t)rows * (size_t)cols / 32;
+  int64_t mnp, kp;
+  padded_extents(rows, cols, axis, &mnp, &kp);
+  *codes_bytes = (size_t)mnp * (size_t)kp / 2;
+  *scales_bytes = (size_t)mnp * (size_t)kp / 32;
   return MX_OK;
 }
 
@@ -81,7 +100,10 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
   if (!empty) {
     if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return MX_ERR_NULL;
     if (ld < cols) return MX_ERR_SHAPE;
-    if (!aligned(codes, 16)) return MX_ERR_ALIGN;
+    if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
+    int64_t mnp, kp;
+    padded_extents(rows, cols, axis, &mnp, &kp);
+    if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
     if (axis == 1) {
       if (ld % 8 != 0 || !aligned(x_bf16, 16)) return MX_ERR_ALIGN;
     } else {

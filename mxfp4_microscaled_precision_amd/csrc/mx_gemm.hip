@@ -90,37 +90,34 @@ __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_ba
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel (K % 128 == 0): 256x256 block tile, K = 256 FP4 elements (128
-// bytes) per stage, two LDS stages. Four waves in a 2x2 grid, 128x128 per
-// wave = 8x8 MFMA tiles (256 fp32 accumulators per lane).
+// 256x256 block tile, eight waves (two per SIMD) in a 2x4 grid, 128x64 per
+// wave = 8x4 MFMA tiles (128 fp32 accumulators per lane); two waves per SIMD
+// let one wave's MFMAs cover the other's stalls.
 //
-// Codes and scales move global -> LDS with direct-to-LDS buffer loads (no
-// register staging); stage s + 1 is in flight while stage s is multiplied.
-// Rows past M / N and K chunks past K read as zero through the buffer range
-// check; zero codes contribute exactly zero whatever their scale.
-//
-// LDS codes layout: [row][8 chunks of 16 B]; logical chunk c of row r sits in
-// slot c ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1). The 16 rows one ds_read_b128
-// touches (rows of one 16-row MFMA tile, same logical chunk) then fall in
-// distinct bank groups for 32- and 64-bank LDS alike, and since g only
-// depends on r & 15 every tile's fragment address is one base register plus
-// an immediate. A DMA load writes lane i's 16 bytes to slot i of the wave's
-// destination, so the swizzle is applied by choosing which global chunk each
-// lane fetches. Scales layout: [row][8 bytes], byte q = K block q of the stage.
+// Operands are in the tiled layout the quantizer writes: a 1 KB tile holds 16
+// rows x 128 K elements as [32-block c][row r][16 B], which is exactly the
+// 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; scales of a
+// 128-wide K slice are one contiguous run of 4 bytes per row. K advances one
+// slice per stage through a ring of four LDS stage buffers with three stages
+// in flight. Every copy is a direct-to-LDS load of one contiguous span (a
+// 1 KB tile or 256 bytes of scales), and every LDS fragment read is one
+// contiguous 1 KB span, the only pattern gfx950's LDS serves at its full 256
+// bytes per clock (measured: a row-major layout takes 4x and an XOR-swizzled
+// one 2x the cycles; gathering rows from a row-major operand made the copies
+// 2.5x slower). Tiles past the operand's padded extent read as zero through
+// the buffer range check; padded rows and K blocks hold encoded zeros.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBKBytes = 128;                      // 256 FP4 elements
-constexpr int kStageA = kBM * kBKBytes;            // 32 KB
-constexpr int kStageB = kBN * kBKBytes;            // 32 KB
-constexpr int kStageSA = kBM * 8;                  // 2 KB
-constexpr int kStageSB = kBN * 8;                  // 2 KB
+constexpr int kThreads = 512;
+constexpr int kStageA = kBM * 64;                  // 16 tiles of 1 KB
+constexpr int kStageB = kBN * 64;
+constexpr int kStageSA = kBM * 4;                  // 1 KB of scales
+constexpr int kStageSB = kBN * 4;
 constexpr int kStageBytes = kStageA + kStageB + kStageSA + kStageSB;
+constexpr int kRing = 4;                           // stage buffers (136 KB)
+constexpr int kAhead = kRing - 1;                  // stages in flight
 constexpr int kGroupM = 8;                         // tile rows per ordering group
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-}
 
 // Tile index -> (tile_m, tile_n): workgroups are dispatched round-robin over
 // the 8 XCDs, so consecutive ids are first regrouped per XCD, then ordered in
@@ -140,185 +137,121 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t tm, int64_t tn,
   *ni = r / gm;
 }
 
+// Each wave issues five DMA instructions per stage (two tiles of A, two of B,
+// one scale run). Wait until at most `later` stages' worth are outstanding.
+__device__ __forceinline__ void wait_stages(int later) {
+  if (later >= 2)
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (later == 1)
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int OUT_BF16>
-__global__ __launch_bounds__(256, 1) void gemm_lds_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7
+  const int wm = wave >> 2, wn = wave & 3;                     // 2 x 4 wave grid
   const int64_t tm = (g.M + kBM - 1) / kBM, tn = (g.N + kBN - 1) / kBN;
   int64_t mi, ni;
   tile_coords(blockIdx.x, tm, tn, &mi, &ni);
   const int m0 = (int)(mi * kBM), n0 = (int)(ni * kBN);
-  const int M = (int)g.M, N = (int)g.N;
-  const int kbytes = (int)(g.K >> 1);
-  const int kblocks = (int)(g.K >> 5);
-  const int nstage = (kblocks + 7) >> 3;
-
-  const int a_bytes = M * kbytes, b_bytes = N * kbytes;
-  const int sa_bytes = M * kblocks, sb_bytes = N * kblocks;
+  const int mp = (int)((g.M + 15) & ~15LL), np = (int)((g.N + 15) & ~15LL);   // padded rows
+  const int nslices = (int)((g.K + 127) >> 7);
+  const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
+  const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
   const v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
   const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
-  const v4i rsrc_sa = make_rsrc(g.a_scales, (uint32_t)sa_bytes);
-  const v4i rsrc_sb = make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+  const v4i rsrc_s = wave < 4 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
+                              : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
-  // Codes DMA: wave w fills stage rows [64 w, 64 w + 64), eight rows per load
-  // j; lane -> row 64 w + 8 j + (lane >> 3), slot lane & 7, whose logical
-  // chunk is (lane & 7) ^ (lane >> 3) ^ (j & 1).
-  const int lrow = lane >> 3;
-  const int c0 = (lane & 7) ^ lrow;
-  const int arow0 = m0 + wave * 64 + lrow;
-  const int brow0 = n0 + wave * 64 + lrow;
-  // Scales DMA: two 4-byte loads per operand per wave; lane -> row
-  // 64 w + 32 q + (lane >> 1), half (lane & 1) of the stage's 8 scale bytes.
-  const int srow0 = wave * 64 + (lane >> 1);
-  const int shalf = lane & 1;
+  // Codes: wave w copies row groups 2w, 2w + 1 of the block's A and B rows;
+  // group G, slice s is the 1 KB at (G * nslices + s) * 1 KB. Groups past the
+  // padded extent (wave-uniform test) load from the buffer end, i.e. zeros.
+  const int ga = (m0 >> 4) + wave * 2, gb = (n0 >> 4) + wave * 2;
+  const int a_lane = ga * nslices * 1024 + lane * 16;
+  const int b_lane = gb * nslices * 1024 + lane * 16;
+  // Scales: waves 0..3 copy A's rows 64 w .. 64 w + 63, waves 4..7 B's;
+  // rows past the padded extent load zeros.
+  const int s_rows = wave < 4 ? mp : np;
+  const int s_row = (wave < 4 ? m0 : n0) + (wave & 3) * 64 + lane;
+  const int s_bytes = wave < 4 ? sa_bytes : sb_bytes;
+  const int s_lane = s_row * 4;
+  const uint32_t s_lds = (uint32_t)(kStageA + kStageB + (wave < 4 ? 0 : kStageSA) + (wave & 3) * 256);
 
   auto issue = [&](int s, int buf) {
     const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
+    int al = a_lane, bl = b_lane, sl = s_lane;
+    asm volatile("" : "+v"(al), "+v"(bl), "+v"(sl));     // recompute, do not hoist
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int chunk = c0 ^ (j & 1);
-      const bool kval = s * 8 + chunk < kblocks;
-      const int ra = arow0 + 8 * j, rb = brow0 + 8 * j;
-      const int koff = s * kBKBytes + chunk * 16;
-      const int ao = (kval && ra < M) ? ra * kbytes + koff : a_bytes;
-      const int bo = (kval && rb < N) ? rb * kbytes + koff : b_bytes;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (wave * 64 + 8 * j) * kBKBytes);
-      dma_load16(rsrc_a, ao, dst);
-      dma_load16(rsrc_b, bo, dst + kStageA);
+    for (int j = 0; j < 2; ++j) {
+      const int off = (j * nslices + s) * 1024;          // wave-uniform
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((wave * 2 + j) * 1024));
+      dma_load16(rsrc_a, (ga + j) * 16 < mp ? al + off : a_bytes, dst);
+      dma_load16(rsrc_b, (gb + j) * 16 < np ? bl + off : b_bytes, dst + kStageA);
     }
-    const bool sval = s * 8 + shalf * 4 < kblocks;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = srow0 + 32 * q;
-      const int ra = m0 + r, rb = n0 + r;
-      const int so = s * 8 + shalf * 4;
-      const int sao = (sval && ra < M) ? ra * kblocks + so : sa_bytes;
-      const int sbo = (sval && rb < N) ? rb * kblocks + so : sb_bytes;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          stage + kStageA + kStageB + (wave * 64 + 32 * q) * 8);
-      dma_load4(rsrc_sa, sao, dst);
-      dma_load4(rsrc_sb, sbo, dst + kStageSA);
-    }
+    dma_load4(rsrc_s, s_row < s_rows ? sl + s * s_rows * 4 : s_bytes,
+              __builtin_amdgcn_readfirstlane(stage + s_lds));
   };
 
-  v4f acc[8][8];
+  v4f acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int lr = lane & 15;      // row within a 16-row MFMA tile
-  const int lg = lane >> 4;      // 32-element K group within a 128-wide K slice
-
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
-    if (s + 1 < nstage) issue(s + 1, (s + 1) & 1);
-    const uint8_t *base = smem + (s & 1) * kStageBytes;
-    const uint8_t *sA = base;
-    const uint8_t *sB = base + kStageA;
-    const uint8_t *sSA = base + kStageA + kStageB;
-    const uint8_t *sSB = sSA + kStageSA;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // tile i's rows are base row + 16 i, and swz only depends on the row
-      // within the tile, so one address per operand serves all eight tiles
-      const uint8_t *pa = sA + (wm * 128 + lr) * kBKBytes + swz(lr, h * 4 + lg) * 16;
-      const uint8_t *pb = sB + (wn * 128 + lr) * kBKBytes + swz(lr, h * 4 + lg) * 16;
-      const uint8_t *psa = sSA + (wm * 128 + lr) * 8 + h * 4 + lg;
-      const uint8_t *psb = sSB + (wn * 128 + lr) * 8 + h * 4 + lg;
-      uint4 af[8], bf[8];
-      uint32_t sa[8], sb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        af[i] = *reinterpret_cast<const uint4 *>(pa + i * 16 * kBKBytes);
-        bf[i] = *reinterpret_cast<const uint4 *>(pb + i * 16 * kBKBytes);
-        sa[i] = psa[i * 16 * 8];
-        sb[i] = psb[i * 16 * 8];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_fp4(af[i], bf[j], acc[i][j], sa[i], sb[j]);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      store_tile<OUT_BF16>(g, acc[i][j], (int64_t)m0 + wm * 128 + i * 16 + 4 * lg,
-                           (int64_t)n0 + wn * 128 + j * 16 + lr);
-}
-
-// ---------------------------------------------------------------------------
-// General-K kernel (any K % 32 == 0): 128x128 block tile, four waves of 64x64,
-// operands loaded from global memory straight into the MFMA register layout.
-// Rows past M / N are clamped for loading and masked on store; K slices past
-// K load zero codes.
-// ---------------------------------------------------------------------------
-template <int OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_direct_kernel(GemmArgs g) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t m_base = (int64_t)blockIdx.y * 128 + (wave >> 1) * 64;
-  const int64_t n_base = (int64_t)blockIdx.x * 128 + (wave & 1) * 64;
-  const int64_t kbytes = g.K >> 1;
-  const int64_t kblocks = g.K >> 5;
-  const int row_in = lane & 15;
-  const int kgrp = lane >> 4;
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  int64_t arow[4], brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = min(m_base + 16 * i + row_in, g.M - 1);
-    brow[i] = min(n_base + 16 * i + row_in, g.N - 1);
-  }
+  const int lr = lane & 15;      // row within a 16-row MFMA tile
+  const int lg = lane >> 4;      // 32-element K block within the slice
 
-  for (int64_t k0 = 0; k0 < g.K; k0 += 128) {
-    const int64_t kb = (k0 >> 5) + kgrp;
-    const bool kval = kb < kblocks;
-    uint4 a[4], b[4];
-    uint32_t sa[4], sb[4];
+  for (int p = 0; p < kAhead && p < nslices; ++p) issue(p, p);
+  for (int s = 0; s < nslices; ++s) {
+    wait_stages(min(kAhead - 1, nslices - 1 - s));  // this wave's part of stage s landed
+    __syncthreads();                                 // every wave's part; buffer of s-1 free
+    if (s + kAhead < nslices) issue(s + kAhead, (s + kAhead) % kRing);
+    const uint8_t *base = smem + (s % kRing) * kStageBytes;
+    const uint8_t *pa = base + (wm * 8) * 1024 + lane * 16;
+    const uint8_t *pb = base + kStageA + (wn * 4) * 1024 + lane * 16;
+    // scale bytes of each tile row; the MFMA reads byte 0 of its scale
+    // operand, so a lane-dependent shift selects K block lg
+    const uint8_t *psa = base + kStageA + kStageB + (wm * 128 + lr) * 4;
+    const uint8_t *psb = base + kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4;
+    // B's four fragments stay resident for the stage; A's stream through
+    // with the next one prefetched while the current row's MFMAs run.
+    uint4 bf[4];
+    uint32_t sb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kval) {
-        a[i] = *reinterpret_cast<const uint4 *>(g.a_codes + arow[i] * kbytes + kb * 16);
-        sa[i] = g.a_scales[arow[i] * kblocks + kb];
-        b[i] = *reinterpret_cast<const uint4 *>(g.b_codes + brow[i] * kbytes + kb * 16);
-        sb[i] = g.b_scales[brow[i] * kblocks + kb];
-      } else {
-        a[i] = make_uint4(0, 0, 0, 0);
-        b[i] = make_uint4(0, 0, 0, 0);
-        sa[i] = 127u;
-        sb[i] = 127u;
-      }
+    for (int j = 0; j < 4; ++j) {
+      bf[j] = *reinterpret_cast<const uint4 *>(pb + j * 1024);
+      sb[j] = *reinterpret_cast<const uint32_t *>(psb + j * 16 * 4) >> (8 * lg);
     }
+    uint4 af = *reinterpret_cast<const uint4 *>(pa);
+    uint32_t sa = *reinterpret_cast<const uint32_t *>(psa) >> (8 * lg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      uint4 af_next = af;
+      uint32_t sa_next = sa;
+      if (i + 1 < 8) {
+        af_next = *reinterpret_cast<const uint4 *>(pa + (i + 1) * 1024);
+        sa_next = *reinterpret_cast<const uint32_t *>(psa + (i + 1) * 16 * 4) >> (8 * lg);
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(a[i], b[j], acc[i][j], sa[i], sb[j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(af, bf[j], acc[i][j], sa, sb[j]);
+      af = af_next;
+      sa = sa_next;
+    }
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      store_tile<OUT_BF16>(g, acc[i][j], m_base + 16 * i + 4 * kgrp, n_base + 16 * j + row_in);
+      store_tile<OUT_BF16>(g, acc[i][j], (int64_t)m0 + wm * 128 + i * 16 + 4 * lg,
+                           (int64_t)n0 + wn * 64 + j * 16 + lr);
 }
 
 template <int OUT_BF16>
@@ -343,18 +276,10 @@ hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
     return g.out_bf16 ? launch(fill_zero_kernel<1>, grid, dim3(256), 0, stream, g)
                       : launch(fill_zero_kernel<0>, grid, dim3(256), 0, stream, g);
   }
-  // The LDS kernel addresses each operand through 32-bit buffer offsets.
-  const bool fits32 = g.M * (g.K >> 1) < ((int64_t)1 << 31) &&
-                      g.N * (g.K >> 1) < ((int64_t)1 << 31);
-  if (g.K % 128 == 0 && fits32) {
-    const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)tiles);
-    return g.out_bf16 ? launch(gemm_lds_kernel<1>, grid, dim3(256), 0, stream, g)
-                      : launch(gemm_lds_kernel<0>, grid, dim3(256), 0, stream, g);
-  }
-  const dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128));
-  return g.out_bf16 ? launch(gemm_direct_kernel<1>, grid, dim3(256), 0, stream, g)
-                    : launch(gemm_direct_kernel<0>, grid, dim3(256), 0, stream, g);
+  const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
+  const dim3 grid((unsigned)tiles);
+  return g.out_bf16 ? launch(gemm_tiled_kernel<1>, grid, dim3(kThreads), 0, stream, g)
+                    : launch(gemm_tiled_kernel<0>, grid, dim3(kThreads), 0, stream, g);
 }
 
 }  // namespace mx

@@ -6,7 +6,8 @@
 //   1. widen bf16 to fp32 (exact);
 //   2. random-sign option: negate x_k where Philox bit 31 of index k is set;
 //   3. rotation: fp32 radix-2 butterfly, strides 1, 2, 4, 8, 16 (lower index
-//      a+b, upper a-b), then one multiply by fp32(1/sqrt 32);
+//      a+b, upper a-b), then one multiply by fp32(1/sqrt 32) (folded into
+//      the scale multiply where that is bit-identical, see quantize_block);
 //   4. amax over |y| (on the fp32 bit patterns, so NaN/Inf are seen);
 //   5. E8M0 exponent e = clamp(floor(log2 amax) - 2, -127, 127);
 //   6. t = fp32(y * 2^-e); E2M1 magnitude by nearest-even or stochastic
@@ -16,10 +17,9 @@
 // The whole block lives in one lane's registers, so every butterfly stage is
 // in-lane and the stage order above is the instruction order.
 //
-// Output layout is reduction-major for both axes: axis 1 writes [rows][cols/2]
-// codes and [rows][cols/32] scales; axis 0 writes the transposed tensor,
-// [cols][rows/2] codes and [cols][rows/32] scales, which is the operand order
-// the FP4 matrix cores consume.
+// Output layout is the tiled, reduction-major operand layout the GEMM streams
+// (see below); axis 0 writes the transposed tensor, so both GEMM operands are
+// always reduction-major.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,7 +32,10 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void fwht32(float (&y)[32]) {
+// Unnormalised butterfly: h = H32 x in fp32, strides 1, 2, 4, 8, 16, lower
+// index a + b, upper a - b. The normalisation y = fl32(h * c) is folded into
+// the scale multiply of quantize_block.
+__device__ __forceinline__ void butterfly32(float (&y)[32]) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -45,40 +48,69 @@ __device__ __forceinline__ void fwht32(float (&y)[32]) {
       }
     }
   }
-  const float c = bits_f(kInvSqrt32Bits);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] = __fmul_rn(y[i], c);
 }
 
-// Quantize one 32-element block held in y. For stochastic rounding the 24-bit
-// uniform of element i is produced by u24_of(i). Writes 16 code bytes (as 4
-// dwords) and returns the scale byte.
-template <int RND, typename U24Fn>
-__device__ __forceinline__ uint32_t quantize_block(const float (&y)[32], uint32_t (&out)[4],
+// Quantize one 32-element block. v holds the butterfly output h (ROT) or the
+// input x (!ROT). The rotated value is y = fl32(h * c) with c = fp32(1/sqrt 32).
+//
+//  * amax: max |y| = fl32(max |h| * c), since rounding is monotonic; taken on
+//    the fp32 bit patterns, so a NaN or Inf anywhere marks the block.
+//  * scale: e from amax; t = fl32(y * 2^-e). For e <= 123, c_e = c * 2^-e is
+//    an exact normal fp32 number and t = fl32(h * c_e) equals fl32(y * 2^-e)
+//    bit for bit (a power-of-two scaling commutes with rounding unless t is
+//    subnormal, and a subnormal t encodes as a signed zero either way). For
+//    e > 123 the two multiplies are done as written.
+//  * RNE: v_cvt_scalef32_pk_fp4_f32 at scale 1.0, which rounds to nearest
+//    even and saturates at +-6 exactly like the threshold rule (checked over
+//    every fp32 pattern); two elements per instruction, element 2j in the low
+//    nibble. SR: integer rule of e2m1_sr_mag with the Philox uniform.
+template <int ROT, int RND, typename U24Fn>
+__device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_t (&out)[4],
                                                    U24Fn u24_of) {
   uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(y[i]) & 0x7FFFFFFFu);
+  for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
   if (amax >= 0x7F800000u) {  // a NaN or Inf in the block
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = 0u;
     return 0xFFu;
   }
+  const float c = bits_f(kInvSqrt32Bits);
+  if (ROT) amax = f_bits(__fmul_rn(bits_f(amax), c));
   const int e = block_exponent(amax);
-  const float p = pow2_neg(e);
+  float t[32];
+  if (!ROT) {
+    const float p = pow2_neg(e);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = 0u;
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], p);
+  } else if (e <= 123) {
+    const float ce = __fmul_rn(c, pow2_neg(e));   // exact: c * 2^-e is a normal number
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t yb = f_bits(y[i]);
-    const uint32_t ab = f_bits(__fmul_rn(y[i], p)) & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (RND == MX_K_ROUND_SR)
-      mag = e2m1_sr_mag(ab, u24_of(i));
-    else
-      mag = e2m1_rne_mag(ab);
-    const uint32_t code = mag | ((yb >> 28) & 8u);
-    out[i >> 3] |= code << (4 * (i & 7));
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], ce);
+  } else {
+    const float p = pow2_neg(e);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], c), p);
+  }
+  if (RND == MX_K_ROUND_SR) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t tb = f_bits(t[i]);
+      const uint32_t code = e2m1_sr_mag(tb & 0x7FFFFFFFu, u24_of(i)) | ((tb >> 28) & 8u);
+      out[i >> 3] |= code << (4 * (i & 7));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0u;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[8 * j + 0], t[8 * j + 1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[8 * j + 2], t[8 * j + 3], 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[8 * j + 4], t[8 * j + 5], 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, t[8 * j + 6], t[8 * j + 7], 1.0f, 3);
+      out[j] = w;
+    }
   }
   return (uint32_t)(e + 127);
 }
@@ -96,151 +128,178 @@ __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// axis = 1: blocks run along a row; one lane per block, 64 contiguous bf16
-// bytes in, 16 code bytes + 1 scale byte out.
+// Output layout (tiled, see mx_qtensor in mxfp4.h): the operand is viewed
+// reduction-major, [MN, K], zero-padded to [MNp, Kp] (MNp multiple of 16, Kp
+// of 128). Codes: tile (g, q) = rows 16g.., K elements 128q.. is 1 KB at
+// (g * Kp/128 + q) * 1024, block c of row r at c * 256 + r * 16 inside it.
+// Scales: [Kp/128][MNp][4]. Padding positions hold the encoding of zeros
+// (codes 0, scale code 0).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t code_offset(int64_t mn, int64_t kb, int64_t nslices) {
+  return ((mn >> 4) * nslices + (kb >> 2)) * 1024 + (kb & 3) * 256 + (mn & 15) * 16;
+}
+__device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t mnp) {
+  return ((kb >> 2) * mnp + mn) * 4 + (kb & 3);
+}
+
+// ---------------------------------------------------------------------------
+// axis = 1 (blocks run along a source row): one wave per output tile; lane l
+// owns row (l & 15), block (l >> 4) of the tile: 64 contiguous bf16 bytes in,
+// 16 code bytes out at tile + 16 l (the wave writes its 1 KB tile in one go).
 // ---------------------------------------------------------------------------
 template <int ROT, int RND>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
     uint32_t seed_hi) {
-  const int64_t nblk = cols >> 5;
-  const int64_t total = rows * nblk;
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= total) return;
-  const int64_t r = b / nblk;
-  const int64_t kb = b - r * nblk;
+  const int64_t mnp = (rows + 15) & ~(int64_t)15;
+  const int64_t nslices = (cols + 127) >> 7;
+  const int64_t ntiles = (mnp >> 4) * nslices;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= ntiles) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t g = tile / nslices;
+  const int64_t q = tile - g * nslices;
+  const int64_t r = g * 16 + (lane & 15);
+  const int64_t kb = q * 4 + (lane >> 4);
+  const bool valid = r < rows && (kb << 5) < cols;
 
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(x + r * ld + (kb << 5));
-  u32x4 v[4];
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+  uint32_t s = 0u;                                  // padding: zero codes, scale code 0
+  if (valid) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + r * ld + (kb << 5));
+    u32x4 v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + j);
-  float y[32];
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + j);
+    float y[32];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t d[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      y[8 * j + 2 * t] = bits_f(d[t] << 16);
-      y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+      for (int t = 0; t < 4; ++t) {
+        y[8 * j + 2 * t] = bits_f(d[t] << 16);
+        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+      }
     }
+    if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)(kb << 5), seed_lo);
+    if (ROT != MX_K_ROT_NONE) butterfly32(y);
+    // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
+    const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
+    U4 w{0u, 0u, 0u, 0u};
+    auto u24_of = [&](int i) -> uint32_t {
+      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
+      return pick_word(w, (uint32_t)(i & 3)) >> 8;
+    };
+    s = quantize_block<ROT != MX_K_ROT_NONE, RND>(y, out, u24_of);
   }
-  if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)(kb << 5), seed_lo);
-  if (ROT != MX_K_ROT_NONE) fwht32(y);
-
-  // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
-  const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
-  U4 w{0u, 0u, 0u, 0u};
-  auto u24_of = [&](int i) -> uint32_t {
-    if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
-    return pick_word(w, (uint32_t)(i & 3)) >> 8;
-  };
-  uint32_t out[4];
-  const uint32_t s = quantize_block<RND>(y, out, u24_of);
-  *reinterpret_cast<uint4 *>(codes + r * (cols >> 1) + (kb << 4)) =
+  *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
       make_uint4(out[0], out[1], out[2], out[3]);
-  scales[r * nblk + kb] = (uint8_t)s;
+  scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
 }
 
 // ---------------------------------------------------------------------------
-// axis = 0: blocks run down a column. A lane owns a column pair (c0, c0 + 1)
-// and walks `rb` consecutive 32-row blocks; each row is one coalesced 4-byte
-// load per lane (256 contiguous bytes per wave). Output is transposed:
-// codes [cols][rows/2], scales [cols][rows/32].
+// axis = 0 (blocks run down a source column; the output is the transposed
+// operand): a lane owns a column pair (c0, c0 + 1) = operand rows, and walks
+// `rb` consecutive 32-row blocks; each source row is one coalesced 4-byte
+// load per lane (256 contiguous bytes per wave). Eight lanes cover the 16
+// operand rows of one tile, so each store instruction writes whole 256-byte
+// block rows of eight tiles.
 // ---------------------------------------------------------------------------
 template <int ROT, int RND>
 __global__ __launch_bounds__(256) void quant_axis0_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
     uint32_t seed_hi, int rb, int pair_loads) {
+  const int64_t mnp = (cols + 15) & ~(int64_t)15;
+  const int64_t nslices = (rows + 127) >> 7;
+  const int64_t nkb_pad = nslices * 4;
+  const int64_t nkb = rows >> 5;
   const int64_t cp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t c0 = cp * 2;
-  if (c0 >= cols) return;
-  const bool two = (c0 + 1) < cols;
-  const int64_t nkb = rows >> 5;
+  if (c0 >= mnp) return;
+  const bool has_a = c0 < cols;
+  const bool has_b = (c0 + 1) < cols;
   const int64_t kb_begin = (int64_t)blockIdx.y * rb;
-  const int64_t kb_end = min(nkb, kb_begin + rb);
-  const int64_t code_ld = rows >> 1;
+  const int64_t kb_end = min(nkb_pad, kb_begin + rb);
 
   for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
-    float ya[32], yb[32];
-    const uint16_t *src = x + (kb << 5) * ld + c0;
-    if (two && pair_loads) {   // rows 4-byte aligned: one load per column pair
+    uint32_t oa[4] = {0u, 0u, 0u, 0u}, ob[4] = {0u, 0u, 0u, 0u};
+    uint32_t sa = 0u, sb = 0u;                     // padding: zero codes, scale code 0
+    if (kb < nkb && has_a) {
+      float ya[32], yb[32];
+      const uint16_t *src = x + (kb << 5) * ld + c0;
+      if (has_b && pair_loads) {   // rows 4-byte aligned: one load per column pair
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t d = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t *>(src + (int64_t)i * ld));
-        ya[i] = bits_f(d << 16);
-        yb[i] = bits_f(d & 0xFFFF0000u);
-      }
-    } else if (two) {
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t d = __builtin_nontemporal_load(
+              reinterpret_cast<const uint32_t *>(src + (int64_t)i * ld));
+          ya[i] = bits_f(d << 16);
+          yb[i] = bits_f(d & 0xFFFF0000u);
+        }
+      } else if (has_b) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        ya[i] = bits_f((uint32_t)src[(int64_t)i * ld] << 16);
-        yb[i] = bits_f((uint32_t)src[(int64_t)i * ld + 1] << 16);
-      }
-    } else {
+        for (int i = 0; i < 32; ++i) {
+          ya[i] = bits_f((uint32_t)src[(int64_t)i * ld] << 16);
+          yb[i] = bits_f((uint32_t)src[(int64_t)i * ld + 1] << 16);
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        ya[i] = bits_f((uint32_t)src[(int64_t)i * ld] << 16);
-        yb[i] = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+          ya[i] = bits_f((uint32_t)src[(int64_t)i * ld] << 16);
+          yb[i] = 0.0f;
+        }
       }
+      if (ROT == MX_K_ROT_RAND_SIGN) {
+        apply_signs(ya, (uint32_t)(kb << 5), seed_lo);
+        apply_signs(yb, (uint32_t)(kb << 5), seed_lo);
+      }
+      if (ROT != MX_K_ROT_NONE) {
+        butterfly32(ya);
+        butterfly32(yb);
+      }
+      // stochastic rounding: element (row, c) has L = row * cols + c
+      const int64_t row0 = kb << 5;
+      auto u24_a = [&](int i) -> uint32_t {
+        const uint64_t L = (uint64_t)((row0 + i) * cols + c0);
+        const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
+        return pick_word(w, (uint32_t)(L & 3)) >> 8;
+      };
+      auto u24_b = [&](int i) -> uint32_t {
+        const uint64_t L = (uint64_t)((row0 + i) * cols + c0 + 1);
+        const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
+        return pick_word(w, (uint32_t)(L & 3)) >> 8;
+      };
+      sa = quantize_block<ROT != MX_K_ROT_NONE, RND>(ya, oa, u24_a);
+      if (has_b) sb = quantize_block<ROT != MX_K_ROT_NONE, RND>(yb, ob, u24_b);
     }
-    if (ROT == MX_K_ROT_RAND_SIGN) {
-      apply_signs(ya, (uint32_t)(kb << 5), seed_lo);
-      apply_signs(yb, (uint32_t)(kb << 5), seed_lo);
-    }
-    if (ROT != MX_K_ROT_NONE) {
-      fwht32(ya);
-      fwht32(yb);
-    }
-    // stochastic rounding: element (row, c) has L = row * cols + c
-    const int64_t row0 = kb << 5;
-    auto u24_a = [&](int i) -> uint32_t {
-      const uint64_t L = (uint64_t)((row0 + i) * cols + c0);
-      const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
-      return pick_word(w, (uint32_t)(L & 3)) >> 8;
-    };
-    auto u24_b = [&](int i) -> uint32_t {
-      const uint64_t L = (uint64_t)((row0 + i) * cols + c0 + 1);
-      const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
-      return pick_word(w, (uint32_t)(L & 3)) >> 8;
-    };
-    uint32_t oa[4], ob[4];
-    const uint32_t sa = quantize_block<RND>(ya, oa, u24_a);
-    *reinterpret_cast<uint4 *>(codes + c0 * code_ld + (kb << 4)) =
+    *reinterpret_cast<uint4 *>(codes + code_offset(c0, kb, nslices)) =
         make_uint4(oa[0], oa[1], oa[2], oa[3]);
-    scales[c0 * nkb + kb] = (uint8_t)sa;
-    if (two) {
-      const uint32_t sb = quantize_block<RND>(yb, ob, u24_b);
-      *reinterpret_cast<uint4 *>(codes + (c0 + 1) * code_ld + (kb << 4)) =
-          make_uint4(ob[0], ob[1], ob[2], ob[3]);
-      scales[(c0 + 1) * nkb + kb] = (uint8_t)sb;
-    }
+    *reinterpret_cast<uint4 *>(codes + code_offset(c0 + 1, kb, nslices)) =
+        make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    scales[scale_offset(c0, kb, mnp)] = (uint8_t)sa;
+    scales[scale_offset(c0 + 1, kb, mnp)] = (uint8_t)sb;
   }
 }
 
 template <int ROT, int RND>
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
-    const int64_t total = a.rows * (a.cols >> 5);
-    const int threads = 256;
-    const int64_t blocks = (total + threads - 1) / threads;
-    return launch(quant_axis1_kernel<ROT, RND>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+    const int64_t mnp = (a.rows + 15) & ~(int64_t)15;
+    const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
+    const int64_t blocks = (ntiles + 3) / 4;
+    return launch(quant_axis1_kernel<ROT, RND>, dim3((unsigned)blocks), dim3(256), 0, stream,
                   a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi);
-  } else {
-    const int threads = 256;
-    const int64_t pairs = (a.cols + 1) >> 1;
-    const int64_t gx = (pairs + threads - 1) / threads;
-    const int64_t nkb = a.rows >> 5;
-    const int rb = a.rb > 0 ? a.rb : 4;
-    const int64_t gy = (nkb + rb - 1) / rb;
-    const int pair_loads =
-        (a.ld % 2 == 0) && (reinterpret_cast<uintptr_t>(a.x) % 4 == 0) ? 1 : 0;
-    return launch(quant_axis0_kernel<ROT, RND>, dim3((unsigned)gx, (unsigned)gy), dim3(threads),
-                  0, stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi,
-                  rb, pair_loads);
   }
+  const int threads = 256;
+  const int64_t mnp = (a.cols + 15) & ~(int64_t)15;
+  const int64_t gx = (mnp / 2 + threads - 1) / threads;
+  const int64_t nkb_pad = ((a.rows + 127) >> 7) * 4;
+  const int rb = a.rb > 0 ? a.rb : 4;
+  const int64_t gy = (nkb_pad + rb - 1) / rb;
+  const int pair_loads = (a.ld % 2 == 0) && (reinterpret_cast<uintptr_t>(a.x) % 4 == 0) ? 1 : 0;
+  return launch(quant_axis0_kernel<ROT, RND>, dim3((unsigned)gx, (unsigned)gy), dim3(threads), 0,
+                stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi, rb,
+                pair_loads);
 }
 
 }  // namespace

@@ -56,6 +56,8 @@ What pins each function (tests/test_oracle_*.py, all "not gpu"):
   round_e2m1_sr         unbiasedness over 10^4 seeds; limits f -> 0 and 1.
   quantize_ref          worked one-hot / constant / zero / NaN blocks;
                         re-quantizing a representable block is a fixed point.
+  tile_codes/scales     element-by-element address formula written out in a
+                        test loop; round trip through untile_*.
   dequantize_ref,
   mx_gemm_ref           explicit triple loop and exact fractions.Fraction sums;
                         the rotation cancels in the product.
@@ -86,6 +88,13 @@ __all__ = [
     "dequantize_ref",
     "pack_codes",
     "unpack_codes",
+    "TILE_ROWS",
+    "TILE_K",
+    "padded_extents",
+    "tile_codes",
+    "tile_scales",
+    "untile_codes",
+    "untile_scales",
     "mx_gemm_ref",
     "linear_ref",
     "bf16_round_ref",
@@ -386,6 +395,61 @@ def pack_codes(codes: np.ndarray) -> np.ndarray:
     """Two codes per byte along K: even index in the low nibble."""
     codes = np.asarray(codes, dtype=np.uint8)
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+TILE_ROWS = 16      # reduction-major rows per tile
+TILE_K = 128        # reduction elements per tile (four 32-element blocks)
+
+
+def padded_extents(mn: int, k: int) -> Tuple[int, int]:
+    """Extents of the tiled layout: MN up to a multiple of 16, K of 128."""
+    return -(-mn // TILE_ROWS) * TILE_ROWS, -(-k // TILE_K) * TILE_K
+
+
+def tile_codes(codes: np.ndarray) -> np.ndarray:
+    """Packed codes [MN, K] (one 4-bit code per element) -> tiled byte buffer.
+
+    The operand is zero-padded to [MNp, Kp] (padded_extents; the codes of a
+    zero element are 0) and stored tile by tile: tile (g, q) holds rows
+    16g..16g+15 and K elements 128q..128q+127 at byte offset
+    (g * Kp/128 + q) * 1024; inside a tile, 32-element block c of row r is the
+    16 bytes at c * 256 + r * 16 (two codes per byte, even K index low).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    mn, k = codes.shape
+    mnp, kp = padded_extents(mn, k)
+    full = np.zeros((mnp, kp), np.uint8)
+    full[:mn, :k] = codes
+    packed = pack_codes(full)                                   # [MNp, Kp/2]
+    t = packed.reshape(mnp // TILE_ROWS, TILE_ROWS, kp // TILE_K, 4, 16)   # g r q c byte
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)    # g q c r byte
+
+
+def tile_scales(scales: np.ndarray, k: int) -> np.ndarray:
+    """Scales [MN, K/32] -> tiled buffer [Kp/128][MNp][4] (padding scale code 0,
+    the code of an all-zero block)."""
+    scales = np.asarray(scales, dtype=np.uint8)
+    mn = scales.shape[0]
+    mnp, kp = padded_extents(mn, k)
+    full = np.zeros((mnp, kp // 32), np.uint8)
+    full[:mn, :scales.shape[1]] = scales
+    return np.ascontiguousarray(full.reshape(mnp, kp // TILE_K, 4).transpose(1, 0, 2)).reshape(-1)
+
+
+def untile_codes(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
+    """Inverse of tile_codes: tiled bytes -> codes [MN, K]."""
+    mnp, kp = padded_extents(mn, k)
+    t = np.asarray(buf, np.uint8)[: mnp * kp // 2].reshape(mnp // TILE_ROWS, kp // TILE_K, 4,
+                                                           TILE_ROWS, 16)
+    packed = t.transpose(0, 3, 1, 2, 4).reshape(mnp, kp // 2)
+    return unpack_codes(packed)[:mn, :k]
+
+
+def untile_scales(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
+    """Inverse of tile_scales: tiled bytes -> scales [MN, K/32]."""
+    mnp, kp = padded_extents(mn, k)
+    t = np.asarray(buf, np.uint8)[: mnp * kp // 32].reshape(kp // TILE_K, mnp, 4)
+    return t.transpose(1, 0, 2).reshape(mnp, kp // 32)[:mn, : k // 32]
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:

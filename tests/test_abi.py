@@ -39,8 +39,12 @@ def test_version_and_status_strings():
 
 def test_quantize_sizes():
     assert mx.quantize_sizes(8192, 4096, 1) == (8192 * 4096 // 2, 8192 * 4096 // 32)
-    assert mx.quantize_sizes(256, 96, 0) == (256 * 96 // 2, 256 * 96 // 32)
+    # tiled layout: MN padded to 16, K to 128
+    assert mx.quantize_sizes(256, 96, 0) == (96 * 256 // 2, 96 * 256 // 32)
+    assert mx.quantize_sizes(37, 160, 1) == (48 * 256 // 2, 48 * 256 // 32)
+    assert mx.quantize_sizes(160, 37, 0) == (48 * 256 // 2, 48 * 256 // 32)
     assert mx.quantize_sizes(0, 0, 1) == (0, 0)
+    assert mx.quantize_sizes(0, 64, 1) == (0, 0)
     for args, code in [((64, 48, 1), -2), ((48, 64, 0), -2), ((64, 64, 2), -4),
                        ((-1, 64, 1), -2)]:
         with pytest.raises(mx.MxError) as ei:
@@ -72,6 +76,8 @@ def test_quantize_rejects_before_launch():
     assert _q(lib, P + 2, 64, 64, 64) == -3              # x misaligned (axis 1)
     assert _q(lib, P + 1, 64, 64, 64, axis=0) == -3      # x odd address (axis 0)
     assert _q(lib, P, 64, 64, 64, codes=P + 4) == -3     # codes misaligned
+    assert _q(lib, P, 64, 64, 64, scales=P + 2) == -3    # scales misaligned
+    assert _q(lib, P, 1 << 17, 1 << 14, 1 << 14) == -6   # codes of 1 GiB: unsupported
     assert _q(lib, None, 64, 64, 64) == -1
     assert _q(lib, P, 64, 64, 64, codes=None) == -1
     assert _q(lib, P, 64, 64, 64, scales=None) == -1

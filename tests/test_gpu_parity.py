@@ -25,12 +25,16 @@ def _sync():
 
 
 def _check_q(q_gpu, ref, what=""):
+    """Byte-exact comparison of the GPU's tiled buffers with the oracle's
+    codes and scales packed into the same tiled layout (padding included)."""
     codes = host_u8(q_gpu.codes)
     scales = host_u8(q_gpu.scales)
-    want_codes = oracle.pack_codes(ref.codes)
-    assert codes.shape == want_codes.shape, what
+    k = ref.codes.shape[1]
+    want_codes = oracle.tile_codes(ref.codes)
+    want_scales = oracle.tile_scales(ref.scales, k)
+    assert codes.shape == want_codes.shape and scales.shape == want_scales.shape, what
     bad = np.count_nonzero(codes != want_codes)
-    bad_s = np.count_nonzero(scales != ref.scales)
+    bad_s = np.count_nonzero(scales != want_scales)
     assert bad == 0 and bad_s == 0, f"{what}: {bad} code bytes, {bad_s} scales differ"
 
 
@@ -244,10 +248,12 @@ def test_full_size_sampled(mx, name, variant):
 
     ra = ref_rows(a_src, ax_a, ms, seed_a)
     rb = ref_rows(b_src, ax_b, ns, seed_b)
-    assert np.array_equal(host_u8(qa.codes[ms]), oracle.pack_codes(ra.codes))
-    assert np.array_equal(host_u8(qa.scales[ms]), ra.scales)
-    assert np.array_equal(host_u8(qb.codes[ns]), oracle.pack_codes(rb.codes))
-    assert np.array_equal(host_u8(qb.scales[ns]), rb.scales)
+    ga = oracle.untile_codes(host_u8(qa.codes), M, qa.k)
+    gsa = oracle.untile_scales(host_u8(qa.scales), M, qa.k)
+    gb = oracle.untile_codes(host_u8(qb.codes), N, qb.k)
+    gsb = oracle.untile_scales(host_u8(qb.scales), N, qb.k)
+    assert np.array_equal(ga[ms], ra.codes) and np.array_equal(gsa[ms], ra.scales)
+    assert np.array_equal(gb[ns], rb.codes) and np.array_equal(gsb[ns], rb.scales)
     C_ref = oracle.mx_gemm_ref(ra, rb)
     got = c.cpu().numpy()[np.ix_(ms, ns)]
     err = rel_fro(got, C_ref)

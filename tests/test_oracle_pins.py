@@ -427,3 +427,29 @@ def test_bf16_round_matches_torch():
     x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, 100000)).astype(np.float32)
     want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.bf16_round_ref(x), want)
+
+
+def test_tiled_layout_addresses_and_roundtrip():
+    """Every element's byte address in the tiled buffer follows the layout
+    formula (written here as an explicit loop), and untile inverts tile."""
+    rng = np.random.default_rng(13)
+    for mn, k in ((37, 160), (16, 128), (5, 32), (33, 256)):
+        codes = rng.integers(0, 16, (mn, k)).astype(np.uint8)
+        scales = rng.integers(0, 255, (mn, k // 32)).astype(np.uint8)
+        tb = oracle.tile_codes(codes)
+        sb = oracle.tile_scales(scales, k)
+        mnp, kp = oracle.padded_extents(mn, k)
+        assert tb.size == mnp * kp // 2 and sb.size == mnp * kp // 32
+        for m in range(mn):
+            for kk in range(0, k, 7):
+                g, r, q, c = m // 16, m % 16, kk // 128, (kk % 128) // 32
+                byte = (g * (kp // 128) + q) * 1024 + c * 256 + r * 16 + (kk % 32) // 2
+                nib = (tb[byte] >> 4) if kk % 2 else (tb[byte] & 15)
+                assert nib == codes[m, kk]
+            for kb in range(k // 32):
+                assert sb[((kb // 4) * mnp + m) * 4 + kb % 4] == scales[m, kb]
+        # padding: zero codes, scale code 0
+        full = oracle.untile_codes(tb, mnp, kp)
+        assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
+        assert np.array_equal(oracle.untile_codes(tb, mn, k), codes)
+        assert np.array_equal(oracle.untile_scales(sb, mn, k), scales)
