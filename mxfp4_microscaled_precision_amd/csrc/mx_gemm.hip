@@ -12,8 +12,10 @@
 // supplies row (l % 16) of A and row (l % 16) of B, K elements
 // [32 * (l / 16), 32 * (l / 16) + 32) as 16 packed bytes (element 2j in the
 // low nibble of byte j), and the E8M0 scale of exactly that 32-element block
-// in byte 0 of its scale operand. Lane l receives C rows 4 * (l / 16) + r,
-// r = 0..3, of column l % 16.
+// in byte 0 of its scale operand; lane l receives rows 4 * (l / 16) + r,
+// r = 0..3, of output column l % 16. The kernel passes B as the first
+// operand, so lane l holds C[l % 16][4 * (l / 16) + r]: four consecutive
+// columns of one row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,17 +45,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Generic epilogue store of one quad: lane (lr, lg) of a 16x16 tile holds
+// C[row][col .. col + 3] with row = tile row + lr, col = tile col + 4 lg.
+// Element-wise and masked, for shapes the row-staged path does not take.
 template <int OUT_BF16>
-__device__ __forceinline__ void store_tile(const GemmArgs &g, const v4f &acc, int64_t row0,
+__device__ __forceinline__ void store_quad(const GemmArgs &g, const v4f &acc, int64_t row,
                                            int64_t col) {
+  if (row >= g.M) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t row = row0 + r;
-    if (row < g.M && col < g.N) {
+    if (col + r < g.N) {
       if (OUT_BF16)
-        reinterpret_cast<uint16_t *>(g.c)[row * g.ldc + col] = f32_to_bf16_rne(acc[r]);
+        reinterpret_cast<uint16_t *>(g.c)[row * g.ldc + col + r] = f32_to_bf16_rne(acc[r]);
       else
-        reinterpret_cast<float *>(g.c)[row * g.ldc + col] = acc[r];
+        reinterpret_cast<float *>(g.c)[row * g.ldc + col + r] = acc[r];
     }
   }
 }
@@ -75,15 +80,16 @@ __device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
 // compiler neither serialises consecutive DMA loads nor waits for them before
 // unrelated LDS reads (it cannot tell LDS destinations apart); the kernel
 // waits for them explicitly (s_waitcnt vmcnt) before the barrier that
-// publishes a stage.
+// publishes a stage. The s_nop covers GFX9's one wait state between an M0
+// write and an LDS DMA that reads it.
 __device__ __forceinline__ void dma_load16(v4i rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "s"(lds_base)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(rsrc), "s"(lds_base)
                : "memory", "m0");
@@ -99,7 +105,8 @@ __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_ba
 // 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; scales of a
 // 128-wide K slice are one contiguous run of 4 bytes per row. K advances one
 // slice per stage through a ring of four LDS stage buffers with three stages
-// in flight. Every copy is a direct-to-LDS load of one contiguous span (a
+// in flight; each stage's copies are spread over its MFMA rows and the next
+// stage's fragments are read while the current one's MFMAs run. Every copy is a direct-to-LDS load of one contiguous span (a
 // 1 KB tile or 256 bytes of scales), and every LDS fragment read is one
 // contiguous 1 KB span, the only pattern gfx950's LDS serves at its full 256
 // bytes per clock (measured: a row-major layout takes 4x and an XOR-swizzled
@@ -135,17 +142,6 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t tm, int64_t tn,
   const int64_t r = id - grp * per_group;
   *mi = first_m + r % gm;
   *ni = r / gm;
-}
-
-// Each wave issues five DMA instructions per stage (two tiles of A, two of B,
-// one scale run). Wait until at most `later` stages' worth are outstanding.
-__device__ __forceinline__ void wait_stages(int later) {
-  if (later >= 2)
-    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else if (later == 1)
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int OUT_BF16>
@@ -184,19 +180,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int s_lane = s_row * 4;
   const uint32_t s_lds = (uint32_t)(kStageA + kStageB + (wave < 4 ? 0 : kStageSA) + (wave & 3) * 256);
 
-  auto issue = [&](int s, int buf) {
+  // DMA instruction `part` (0, 1: A tiles; 2, 3: B tiles; 4: scales) of
+  // stage s into ring buffer buf. Stages past the last slice read zeros, so
+  // every stage issues the same five instructions and the vmcnt bookkeeping
+  // stays uniform.
+  auto issue_part = [&](int s, int buf, int part) {
     const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
-    int al = a_lane, bl = b_lane, sl = s_lane;
-    asm volatile("" : "+v"(al), "+v"(bl), "+v"(sl));     // recompute, do not hoist
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int off = (j * nslices + s) * 1024;          // wave-uniform
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((wave * 2 + j) * 1024));
-      dma_load16(rsrc_a, (ga + j) * 16 < mp ? al + off : a_bytes, dst);
-      dma_load16(rsrc_b, (gb + j) * 16 < np ? bl + off : b_bytes, dst + kStageA);
+    const bool live = s < nslices;
+    if (part < 4) {
+      const int j = part & 1;
+      const bool is_b = part >= 2;
+      int l = is_b ? b_lane : a_lane;
+      asm volatile("" : "+v"(l));
+      const int off = (j * nslices + s) * 1024;
+      const bool ok = live && ((is_b ? gb : ga) + j) * 16 < (is_b ? np : mp);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          stage + (uint32_t)((wave * 2 + j) * 1024 + (is_b ? kStageA : 0)));
+      dma_load16(is_b ? rsrc_b : rsrc_a, ok ? l + off : (is_b ? b_bytes : a_bytes), dst);
+    } else {
+      int l = s_lane;
+      asm volatile("" : "+v"(l));
+      dma_load4(rsrc_s, (live && s_row < s_rows) ? l + s * s_rows * 4 : s_bytes,
+                __builtin_amdgcn_readfirstlane(stage + s_lds));
     }
-    dma_load4(rsrc_s, s_row < s_rows ? sl + s * s_rows * 4 : s_bytes,
-              __builtin_amdgcn_readfirstlane(stage + s_lds));
   };
 
   v4f acc[8][4];
@@ -207,51 +213,144 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
 
   const int lr = lane & 15;      // row within a 16-row MFMA tile
   const int lg = lane >> 4;      // 32-element K block within the slice
+  const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
+  const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
+  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
+  auto ld16 = [&](int buf, uint32_t off) {
+    return *reinterpret_cast<const uint4 *>(smem + buf * kStageBytes + off);
+  };
+  // the MFMA reads byte 0 of its scale operand: shift K block lg's byte there
+  auto ld_scale = [&](int buf, uint32_t off) {
+    return *reinterpret_cast<const uint32_t *>(smem + buf * kStageBytes + off) >> (8 * lg);
+  };
 
-  for (int p = 0; p < kAhead && p < nslices; ++p) issue(p, p);
-  for (int s = 0; s < nslices; ++s) {
-    wait_stages(min(kAhead - 1, nslices - 1 - s));  // this wave's part of stage s landed
-    __syncthreads();                                 // every wave's part; buffer of s-1 free
-    if (s + kAhead < nslices) issue(s + kAhead, (s + kAhead) % kRing);
-    const uint8_t *base = smem + (s % kRing) * kStageBytes;
-    const uint8_t *pa = base + (wm * 8) * 1024 + lane * 16;
-    const uint8_t *pb = base + kStageA + (wn * 4) * 1024 + lane * 16;
-    // scale bytes of each tile row; the MFMA reads byte 0 of its scale
-    // operand, so a lane-dependent shift selects K block lg
-    const uint8_t *psa = base + kStageA + kStageB + (wm * 128 + lr) * 4;
-    const uint8_t *psb = base + kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4;
-    // B's four fragments stay resident for the stage; A's stream through
-    // with the next one prefetched while the current row's MFMAs run.
-    uint4 bf[4];
-    uint32_t sb[4];
+  for (int p = 0; p < kAhead; ++p)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[j] = *reinterpret_cast<const uint4 *>(pb + j * 1024);
-      sb[j] = *reinterpret_cast<const uint32_t *>(psb + j * 16 * 4) >> (8 * lg);
-    }
-    uint4 af = *reinterpret_cast<const uint4 *>(pa);
-    uint32_t sa = *reinterpret_cast<const uint32_t *>(psa) >> (8 * lg);
+    for (int part = 0; part < 5; ++part) issue_part(p, p, part);
+  asm volatile("s_waitcnt vmcnt(10)" ::: "memory");   // this wave's part of stage 0
+  __syncthreads();
+
+  uint4 bf[4], bn[4], a0, a1;
+  uint32_t sb[4], sbn[4], sa[8], san[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf[j] = ld16(0, b_off + j * 1024);
+    sb[j] = ld_scale(0, sb_off + j * 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sa[i] = ld_scale(0, sa_off + i * 64);
+  a0 = ld16(0, a_off);
+  a1 = ld16(0, a_off + 1024);
+
+  // Stage s: 8 rows of 4 MFMAs. A fragments stream two rows ahead. After
+  // row 3 the wave waits for its part of stage s + 1, and the barrier makes
+  // every wave's part visible and frees the buffer of stage s - 1, which
+  // rows 3..7 then refill with stage s + 3 (one DMA instruction per row).
+  // Rows 4..7 also read stage s + 1's B fragments, scales and first two A
+  // rows, so the next stage starts without an LDS round trip.
+  for (int s = 0; s < nslices; ++s) {
+    const int cur = s & 3, nxt = (s + 1) & 3, refill = (s + 3) & 3;
+    uint4 af[8];
+    af[0] = a0;
+    af[1] = a1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint4 af_next = af;
-      uint32_t sa_next = sa;
-      if (i + 1 < 8) {
-        af_next = *reinterpret_cast<const uint4 *>(pa + (i + 1) * 1024);
-        sa_next = *reinterpret_cast<const uint32_t *>(psa + (i + 1) * 16 * 4) >> (8 * lg);
+      if (i + 2 < 8) af[i + 2] = ld16(cur, a_off + (i + 2) * 1024);
+      if (i == 4) {
+        bn[0] = ld16(nxt, b_off);
+        bn[1] = ld16(nxt, b_off + 1024);
+        sbn[0] = ld_scale(nxt, sb_off);
+        sbn[1] = ld_scale(nxt, sb_off + 64);
+      } else if (i == 5) {
+        bn[2] = ld16(nxt, b_off + 2048);
+        bn[3] = ld16(nxt, b_off + 3072);
+        sbn[2] = ld_scale(nxt, sb_off + 128);
+        sbn[3] = ld_scale(nxt, sb_off + 192);
+      } else if (i == 6) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) san[r] = ld_scale(nxt, sa_off + r * 64);
+        a0 = ld16(nxt, a_off);
+      } else if (i == 7) {
+        a1 = ld16(nxt, a_off + 1024);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(af, bf[j], acc[i][j], sa, sb[j]);
-      af = af_next;
-      sa = sa_next;
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af[i], acc[i][j], sb[j], sa[i]);
+      if (i == 3) {
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");   // own part of stage s + 1
+        __syncthreads();
+      }
+      if (i >= 3) issue_part(s + kAhead, refill, i - 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf[j] = bn[j];
+      sb[j] = sbn[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sa[i] = san[i];
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // zero-fill loads past the end
 
+  // Epilogue. Fast path (N and ldc multiples of 8, C 16-byte aligned): the tile goes through the now idle LDS
+  // ring in row-major order and leaves as whole 512-byte (bf16) or 1 KB
+  // (fp32) rows, one 16-byte store per lane, so every store instruction
+  // writes complete cache lines.
+  const bool fast_epi = (g.N & 7) == 0 && (g.ldc & 7) == 0 &&
+                        (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+  if (fast_epi) {
+    constexpr int kEsz = OUT_BF16 ? 2 : 4;
+    constexpr int kRowB = kBN * kEsz;                // bytes of one tile row
+    constexpr int kPitch = kRowB + 16;               // padded LDS row
+    constexpr int kRowsPerPass = OUT_BF16 ? 256 : 128;
+    static_assert(kRowsPerPass * kPitch <= kRing * kStageBytes, "epilogue staging fits the ring");
+    const int64_t rows_left = g.M - m0;
+    const int cols_left = (int)min((int64_t)kBN, g.N - n0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int h = 0; h < 256 / kRowsPerPass; ++h) {
+      __syncthreads();                               // ring (or previous pass) no longer read
+      if (OUT_BF16 || wm == h) {
+        const int rbase = OUT_BF16 ? wm * 128 : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_tile<OUT_BF16>(g, acc[i][j], (int64_t)m0 + wm * 128 + i * 16 + 4 * lg,
-                           (int64_t)n0 + wn * 64 + j * 16 + lr);
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint8_t *p = smem + (rbase + i * 16 + lr) * kPitch + (wn * 64 + j * 16 + 4 * lg) * kEsz;
+            if (OUT_BF16) {
+              uint2 v;
+              v.x = (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
+              v.y = (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+              *reinterpret_cast<uint2 *>(p) = v;
+            } else {
+              *reinterpret_cast<float4 *>(p) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+          }
+      }
+      __syncthreads();
+      // 16 bytes per thread: kRowB / 16 threads per row
+      constexpr int kThrPerRow = kRowB / 16;
+      constexpr int kRowsPerIter = kThreads / kThrPerRow;
+      const int r_in = tid / kThrPerRow, c16 = tid % kThrPerRow;
+#pragma unroll 4
+      for (int r = r_in; r < kRowsPerPass; r += kRowsPerIter) {
+        const int trow = h * kRowsPerPass + r;
+        const int col = c16 * (16 / kEsz);
+        if (trow < rows_left && col < cols_left) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(smem + r * kPitch + c16 * 16);
+          uint8_t *dst = reinterpret_cast<uint8_t *>(g.c) + ((m0 + trow) * g.ldc + n0 + col) * kEsz;
+          *reinterpret_cast<uint4 *>(dst) = v;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store_quad<OUT_BF16>(g, acc[i][j], (int64_t)m0 + wm * 128 + i * 16 + lr,
+                             (int64_t)n0 + wn * 64 + j * 16 + 4 * lg);
+  }
 }
 
 template <int OUT_BF16>

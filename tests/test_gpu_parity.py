@@ -194,6 +194,28 @@ def test_gemm_several_tiles(mx):
     _gemm_case(mx, "fprop", A, B, "hadamard", "rne", 0)
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("pad", [8, 4, 0])
+def test_gemm_strided_out(mx, out_dtype, pad):
+    """Row-strided output: ldc = N + pad. pad 8 (and 0) takes the row-staged
+    epilogue, pad 4 the element-wise one; both must give the contiguous
+    result bit for bit and leave the pad columns untouched."""
+    import torch
+    rng = np.random.default_rng(31 + pad)
+    M, N, K = 300, 264, 384
+    qa = mx.quantize(to_dev(_rand_bits(rng, (M, K))), 1)
+    qb = mx.quantize(to_dev(_rand_bits(rng, (N, K))), 1)
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    ref = mx.linear("fprop", qa, qb, out_dtype)
+    big = torch.full((M, N + pad), -7.0, dtype=dt, device="cuda")
+    got = mx.linear("fprop", qa, qb, out_dtype, out=big[:, :N])
+    _sync()
+    iv = torch.int32 if out_dtype == "f32" else torch.int16
+    assert torch.equal(got.contiguous().view(iv), ref.view(iv))
+    if pad:
+        assert torch.all(big[:, N:] == -7.0).item()
+
+
 def test_gemm_k_zero_writes_zeros(mx):
     import torch
     A = mx.quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), 0)
@@ -255,6 +277,13 @@ def test_full_size_sampled(mx, name, variant):
     assert np.array_equal(ga[ms], ra.codes) and np.array_equal(gsa[ms], ra.scales)
     assert np.array_equal(gb[ns], rb.codes) and np.array_equal(gsb[ns], rb.scales)
     C_ref = oracle.mx_gemm_ref(ra, rb)
-    got = c.cpu().numpy()[np.ix_(ms, ns)]
+    c_host = c.cpu().numpy()
+    got = c_host[np.ix_(ms, ns)]
     err = rel_fro(got, C_ref)
     assert err <= GEMM_TOL, f"{name}/{variant}: rel Frobenius {err:.3e}"
+    if w.out_dtype == "bf16":
+        # the bf16 epilogue over the whole output: RNE of the fp32 result
+        cb = mx.linear(w.op, qa, qb, "bf16")
+        _sync()
+        got_b = cb.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+        assert np.array_equal(got_b, oracle.bf16_round_ref(c_host))
