@@ -32,6 +32,10 @@ METRIC = "MXFP4 linear TFLOP/s incl. Hadamard+quant, Llama-3.1-8B shapes; % MFMA
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+GEMM_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm.hip"
+GEMM_TRAFFIC = "profiles/gemm_{}_traffic.md"
+QUANT_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_quant.hip"
+QUANT_TRAFFIC = "profiles/quant_{}_traffic.md"
 
 
 def parse():
@@ -44,7 +48,8 @@ def parse():
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload/variant and the full block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="repetitions of the whole-workload oracle run (cpu_baseline)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB three "
                          "times (reference for HBM byte counters)")
@@ -137,8 +142,9 @@ class Runner:
 
 
 def time_loop(fn, iters, warmup):
-    """Average ms per call of fn(i), HIP events on the current stream (the
-    stream the library launches on)."""
+    """Average ms per call of fn(i) over `iters` back-to-back calls, between
+    one pair of HIP events on the current stream (the stream the library
+    launches on)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -154,10 +160,10 @@ def time_loop(fn, iters, warmup):
 
 
 def measure(r, steps, warmup):
+    """The timed region: `steps` whole steps (quantize A, quantize B, GEMM)
+    back to back. Then each kernel alone, back to back, for its average
+    launch duration (events between the kernels of a step would add gaps)."""
     import torch
-    t_qa = time_loop(r.quant_a, max(steps, 10), 3)
-    t_qb = time_loop(r.quant_b, max(steps, 10), 3)
-    t_g = time_loop(r.gemm, max(steps, 10), 3)
     for i in range(warmup):
         r.step(i)
     torch.cuda.synchronize()
@@ -171,6 +177,9 @@ def measure(r, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
+    t_qa = time_loop(r.quant_a, max(steps, 10), 3)
+    t_qb = time_loop(r.quant_b, max(steps, 10), 3)
+    t_g = time_loop(r.gemm, max(steps, 10), 3)
     flops = r.flops()
     return {
         "ms_per_step": ms,
@@ -185,12 +194,11 @@ def measure(r, steps, warmup):
     }
 
 
-def cpu_baseline(r, rows):
-    """The oracle on a bounded sample: the first `rows` reduction-major rows of
-    each operand (full K), quantized, then their fp64 GEMM. Per-element
-    quantization time and per-MAC GEMM time are extrapolated to the whole
-    workload and expressed in the metric's unit."""
-    import numpy as np
+def cpu_baseline(r, reps):
+    """The oracle as it stands, on the host cores: the whole workload
+    (quantize both operands, fp64 GEMM of the dequantized operands), `reps`
+    times; the value is the workload's flops over the mean time."""
+    import numpy as np  # noqa: F401
 
     import oracle
     try:
@@ -199,39 +207,49 @@ def cpu_baseline(r, rows):
                             if p.get("user_api") == "blas"] or [1])
     except Exception:
         blas_threads = None
-    ms = min(rows, r.M)
-    ns = min(rows, r.N)
-
-    def sample(src, axis, n, seed):
-        if axis == 1:
-            return oracle.quantize_ref(src[:n], 1, rotate=r.rot, rounding=r.rnd, seed=seed,
-                                       total_cols=src.shape[1])
-        return oracle.quantize_ref(src[:, :n], 0, rotate=r.rot, rounding=r.rnd, seed=seed,
-                                   col_index=np.arange(n), total_cols=src.shape[1])
-
     seed_a = r.seed & 0xFFFFFFFF
-    t0 = time.perf_counter()
-    qa = sample(r.a_src, r.ax_a, ms, seed_a)
-    qb = sample(r.b_src, r.ax_b, ns, seed_a | (1 << 32))
-    t1 = time.perf_counter()
-    oracle.mx_gemm_ref(qa, qb)
-    t2 = time.perf_counter()
-    t_elem = (t1 - t0) / ((ms + ns) * r.K)
-    t_mac = (t2 - t1) / (ms * ns * r.K)
-    est = t_elem * (r.M + r.N) * r.K + t_mac * r.M * r.N * r.K
+    t_q = t_g = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        qa = oracle.quantize_ref(r.a_src, r.ax_a, rotate=r.rot, rounding=r.rnd, seed=seed_a)
+        qb = oracle.quantize_ref(r.b_src, r.ax_b, rotate=r.rot, rounding=r.rnd,
+                                 seed=seed_a | (1 << 32))
+        t1 = time.perf_counter()
+        oracle.mx_gemm_ref(qa, qb)
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        t_g += t2 - t1
+        del qa, qb
+    per = (t_q + t_g) / reps
     return {
-        "value": r.flops() / est / 1e12,
+        "value": round(r.flops() / per / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
         "affinity_cores": len(os.sched_getaffinity(0)),
         "quantizer_threads": 1,
         "kind": "oracle",
-        "sample": (f"oracle quantize of {ms} rows of A and {ns} rows of B (K={r.K}, "
-                   f"{(t1 - t0):.2f} s, NumPy, 1 thread) + fp64 GEMM {ms}x{ns}x{r.K} "
-                   f"({(t2 - t1):.2f} s, BLAS); per-element and per-MAC times "
-                   f"extrapolated to {r.M}x{r.N}x{r.K}"),
-        "sample_seconds": t2 - t0,
+        "sample": (f"whole workload {r.M}x{r.N}x{r.K} x{reps}: oracle quantize of both "
+                   f"operands (NumPy, 1 thread, {t_q / reps:.2f} s) + fp64 GEMM of the "
+                   f"dequantized operands (BLAS, {t_g / reps:.2f} s) per repetition"),
+        "sample_seconds": round(t_q + t_g, 2),
     }
+
+
+def recorded_traffic(kernel_src, summary):
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, kernel_src), "rb") as fh:
+            digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+        with open(os.path.join(ROOT, summary)) as fh:
+            fields = dict(ln.strip()[2:].split(": ", 1) for ln in fh
+                          if ln.startswith("- ") and ": " in ln)
+        if fields.get("kernel source sha256[:16]") != digest:
+            return None
+        return float(fields["traffic bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -283,7 +301,7 @@ def main():
             "peak": PEAK_FP4_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_ach / PEAK_FP4_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(GEMM_SRC, GEMM_TRAFFIC.format(w.name)),
         },
         "quant_roofline": {
             "kernel": f"mx_quant axis {r.ax_a} (operand A)",
@@ -292,7 +310,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(qa_ach / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(QUANT_SRC, QUANT_TRAFFIC.format(w.name)),
         },
         "per_kernel_us": {k: round(res[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
                                                        "t_gemm_us")},
@@ -326,7 +344,7 @@ def main():
         out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(r, args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(r, args.cpu_reps)
     print(json.dumps(out), flush=True)
 
 
