@@ -333,6 +333,10 @@ def main():
                       flush=True)
                 del rr
         out["other_workloads"] = extra
+        wg = WORKLOADS["wgrad_gate_proj"]
+        out["wgrad_gate_proj_quant_error"] = output_mse(mx, wg, [v[0] for v in wg.variants])
+        print(f"[bench] quant error {out['wgrad_gate_proj_quant_error']}", file=sys.stderr,
+              flush=True)
         out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 5))
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
@@ -346,6 +350,36 @@ def main():
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(r, args.cpu_reps)
     print(json.dumps(out), flush=True)
+
+
+def output_mse(mx, wl, variants):
+    """Quantization error at the output of one GEMM: the fp32 MXFP4 result
+    against the fp32 product of the unquantized bf16 operands (torch.matmul on
+    the GPU), as mean squared error and relative Frobenius error."""
+    import torch
+    from datagen import operands_for, workload_tensors
+    t = workload_tensors(wl)
+    a_src, ax_a, b_src, ax_b = operands_for(wl, t)
+    res = {}
+    for label in variants:
+        rr = Runner(mx, wl, label, tensors=t, min_bytes=0)
+        c = torch.empty((rr.M, rr.N), dtype=torch.float32, device="cuda")
+        st = rr.lib.mx_linear(mx.OPS[wl.op], ctypes.byref(rr.qa[0].desc),
+                              ctypes.byref(rr.qb[0].desc), c.data_ptr(), c.stride(0),
+                              mx.OUT_DTYPES["f32"], rr.stream)
+        if st:
+            raise RuntimeError("mx_linear failed")
+        a = rr.A[0].float()
+        b = rr.B[0].float()
+        a = a if ax_a == 1 else a.t().contiguous()        # [M, K]
+        b = b if ax_b == 1 else b.t().contiguous()        # [N, K]
+        ref = torch.matmul(a, b.t().contiguous())
+        d = (c - ref).double()
+        res[label] = {"output_mse": float((d * d).mean()),
+                      "rel_fro": float(d.norm() / ref.double().norm())}
+        del rr, a, b, ref, d, c
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_block(mx, wls, steps):
