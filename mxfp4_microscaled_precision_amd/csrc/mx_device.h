@@ -35,10 +35,11 @@ struct U4 { uint32_t x, y, z, w; };
 __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = 0xD2511F53u * c.x;
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    // full 64-bit products: one v_mad_u64_u32 each gives both halves
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     U4 n;
     n.x = hi1 ^ c.y ^ k0;
     n.y = lo1;
@@ -78,18 +79,11 @@ __device__ __forceinline__ U4 sr_words(uint64_t q, uint32_t seed_lo, uint32_t se
 // (a NaN or Inf in the block) separately.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
-  int E;
-  if (amax_bits >= 0x00800000u) {
-    E = (int)(amax_bits >> 23) - 127;            // normal: biased exponent - 127
-  } else if (amax_bits != 0u) {
-    E = -118 - (int)__clz(amax_bits);            // subnormal: (31 - clz) - 149
-  } else {
-    return -127;
-  }
-  int e = E - 2;                                  // E2M1's largest exponent is 2
-  e = e < -127 ? -127 : e;
-  e = e > 127 ? 127 : e;
-  return e;
+  // floor(log2 amax) = (biased exponent) - 127 for a normal amax. A
+  // subnormal or zero amax has biased exponent 0 and every such value has
+  // floor(log2 amax) - 2 <= -129, so the lower clamp covers it; the largest
+  // finite amax gives 125, inside the upper clamp.
+  return max((int)(amax_bits >> 23) - 129, -127);
 }
 
 // 2^-e as fp32 for e in [-127, 125] (always a normal number there).
@@ -121,6 +115,7 @@ __device__ __forceinline__ uint32_t e2m1_rne_mag(uint32_t ab) {
 // and the division by the power-of-two gap are exact in fp32, as is the
 // comparison with the integer u24 < 2^24. a >= 6 gives 6 (not randomised).
 __device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
+  // index of the lower neighbour lo in {0, .5, 1, 1.5, 2, 3, 4, 6}
   uint32_t idx = 0;
   idx += ab >= 0x3F000000u;  // 0.5
   idx += ab >= 0x3F800000u;  // 1
@@ -129,21 +124,12 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
   idx += ab >= 0x40400000u;  // 3
   idx += ab >= 0x40800000u;  // 4
   idx += ab >= 0x40C00000u;  // 6
-  if (idx >= 7) return 7;
-  // lo and 2^24 / gap for each lower-neighbour index
-  float lo, inv_gap24;
-  switch (idx) {
-    case 0: lo = 0.0f; inv_gap24 = 33554432.0f; break;  // gap 0.5
-    case 1: lo = 0.5f; inv_gap24 = 33554432.0f; break;
-    case 2: lo = 1.0f; inv_gap24 = 33554432.0f; break;
-    case 3: lo = 1.5f; inv_gap24 = 33554432.0f; break;
-    case 4: lo = 2.0f; inv_gap24 = 16777216.0f; break;  // gap 1
-    case 5: lo = 3.0f; inv_gap24 = 16777216.0f; break;
-    default: lo = 4.0f; inv_gap24 = 8388608.0f; break;  // gap 2
-  }
-  const float a = bits_f(ab);
-  const float thr = __fmul_rn(__fsub_rn(a, lo), inv_gap24);
-  return idx + ((float)u24 < thr ? 1u : 0u);
+  // lo and 2^24 / (hi - lo): gap 0.5 below 2, 1 below 4, 2 below 6
+  const float lo = idx < 4 ? 0.5f * (float)idx : (idx < 6 ? (float)idx - 2.0f : 4.0f);
+  const float inv_gap24 = idx < 4 ? 33554432.0f : (idx < 6 ? 16777216.0f : 8388608.0f);
+  const float thr = __fmul_rn(__fsub_rn(bits_f(ab), lo), inv_gap24);
+  const uint32_t up = (float)u24 < thr ? 1u : 0u;
+  return idx >= 7 ? 7u : idx + up;                // a >= 6 saturates (not randomised)
 }
 
 }  // namespace mx

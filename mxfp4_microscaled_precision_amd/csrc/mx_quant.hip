@@ -53,8 +53,8 @@ __device__ __forceinline__ void butterfly32(float (&y)[32]) {
 // Quantize one 32-element block. v holds the butterfly output h (ROT) or the
 // input x (!ROT). The rotated value is y = fl32(h * c) with c = fp32(1/sqrt 32).
 //
-//  * amax: max |y| = fl32(max |h| * c), since rounding is monotonic; taken on
-//    the fp32 bit patterns, so a NaN or Inf anywhere marks the block.
+//  * amax: max |y| = fl32(max |h| * c), since rounding is monotonic; a NaN
+//    or Inf anywhere in the block marks it (see the amax comment below).
 //  * scale: e from amax; t = fl32(y * 2^-e). For e <= 123, c_e = c * 2^-e is
 //    an exact normal fp32 number and t = fl32(h * c_e) equals fl32(y * 2^-e)
 //    bit for bit (a power-of-two scaling commutes with rounding unless t is
@@ -67,14 +67,22 @@ __device__ __forceinline__ void butterfly32(float (&y)[32]) {
 template <int ROT, int RND, typename U24Fn>
 __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_t (&out)[4],
                                                    U24Fn u24_of) {
+  // amax as bits of |v| (a NaN or Inf compares above 0x7f800000). Without
+  // rotation: integer max of |bits|, which sees a lone NaN. With rotation
+  // every output of a block holding a NaN or Inf is itself NaN or Inf, so
+  // the float max of |v| (which skips NaN operands) still lands above
+  // 0x7f800000 for such blocks and equals the integer max for the others.
   uint32_t amax = 0;
+  if (!ROT) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
-  if (amax >= 0x7F800000u) {  // a NaN or Inf in the block
+    for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
+  } else {
+    float m = fabsf(v[0]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = 0u;
-    return 0xFFu;
+    for (int i = 1; i < 31; i += 2) m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
+    amax = f_bits(fmaxf(m, fabsf(v[31])));
   }
+  const bool nonfinite = amax >= 0x7F800000u;
   const float c = bits_f(kInvSqrt32Bits);
   if (ROT) amax = f_bits(__fmul_rn(bits_f(amax), c));
   const int e = block_exponent(amax);
@@ -83,14 +91,19 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
     const float p = pow2_neg(e);
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], p);
-  } else if (e <= 123) {
-    const float ce = __fmul_rn(c, pow2_neg(e));   // exact: c * 2^-e is a normal number
+  } else if (__builtin_expect(!__any(e > 123), 1)) {
+    // c * 2^-e is an exact normal number for e <= 123: one multiply gives
+    // the bits of fl32(fl32(h * c) * 2^-e)
+    const float ce = __fmul_rn(c, pow2_neg(e));
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], ce);
   } else {
-    const float p = pow2_neg(e);
+    // some lane of the wave has |y| >= 2^126: the two multiplies, for all
+    const float ce = __fmul_rn(c, pow2_neg(min(e, 123)));
+    const float m1 = e > 123 ? c : ce;
+    const float m2 = e > 123 ? pow2_neg(e) : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], c), p);
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], m1), m2);
   }
   if (RND == MX_K_ROUND_SR) {
 #pragma unroll
@@ -112,7 +125,84 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
       out[j] = w;
     }
   }
+  if (nonfinite) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = 0u;
+    return 0xFFu;
+  }
   return (uint32_t)(e + 127);
+}
+
+// Scale of one block for the two-multiply form t = fl32(fl32(v * m1) * m2):
+// m1 = c * 2^-e, m2 = 1 when that product is an exact normal number (e <=
+// 123), else m1 = c, m2 = 2^-e (with rotation); m1 = 2^-e, m2 = 1 without.
+// Returns the scale code (0xFF for a block holding a NaN or Inf, detected as
+// in quantize_block).
+template <int ROT>
+__device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1, float &m2) {
+  uint32_t amax = 0;
+  if (!ROT) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
+  } else {
+    float m = fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 31; i += 2) m = fmaxf(fmaxf(m, fabsf(v[i])), fabsf(v[i + 1]));
+    amax = f_bits(fmaxf(m, fabsf(v[31])));
+  }
+  const bool nonfinite = amax >= 0x7F800000u;
+  const float c = bits_f(kInvSqrt32Bits);
+  if (ROT) amax = f_bits(__fmul_rn(bits_f(amax), c));
+  const int e = block_exponent(amax);
+  if (!ROT) {
+    m1 = pow2_neg(e);
+    m2 = 1.0f;
+  } else {
+    m1 = e > 123 ? c : __fmul_rn(c, pow2_neg(min(e, 123)));
+    m2 = e > 123 ? pow2_neg(e) : 1.0f;
+  }
+  return nonfinite ? 0xFFu : (uint32_t)(e + 127);
+}
+
+// Stochastic rounding of a column pair (c0, c0 + 1) of the axis-0 path. The
+// elements of row i have source indices L = L0 + i * cols and L + 1, which
+// one Philox call covers unless L % 4 == 3.
+template <int ROT>
+__device__ __forceinline__ void quantize_pair_sr(const float (&va)[32], const float (&vb)[32],
+                                                 uint32_t (&oa)[4], uint32_t (&ob)[4],
+                                                 uint32_t &sa, uint32_t &sb, uint64_t L0,
+                                                 int64_t cols, uint32_t seed_lo,
+                                                 uint32_t seed_hi) {
+  float m1a, m2a, m1b, m2b;
+  sa = block_scale<ROT>(va, m1a, m2a);
+  sb = block_scale<ROT>(vb, m1b, m2b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) oa[j] = ob[j] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint64_t L = L0 + (uint64_t)i * (uint64_t)cols;
+    const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
+    const uint32_t j = (uint32_t)(L & 3);
+    const uint32_t ua = pick_word(w, j) >> 8;
+    uint32_t ub;
+    if (j == 3) {
+      ub = sr_words((L >> 2) + 1, seed_lo, seed_hi).x >> 8;
+    } else {
+      ub = pick_word(w, j + 1) >> 8;
+    }
+    const uint32_t ta = f_bits(__fmul_rn(__fmul_rn(va[i], m1a), m2a));
+    const uint32_t tb = f_bits(__fmul_rn(__fmul_rn(vb[i], m1b), m2b));
+    oa[i >> 3] |= (e2m1_sr_mag(ta & 0x7FFFFFFFu, ua) | ((ta >> 28) & 8u)) << (4 * (i & 7));
+    ob[i >> 3] |= (e2m1_sr_mag(tb & 0x7FFFFFFFu, ub) | ((tb >> 28) & 8u)) << (4 * (i & 7));
+  }
+  if (sa == 0xFFu) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) oa[j] = 0u;
+  }
+  if (sb == 0xFFu) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ob[j] = 0u;
+  }
 }
 
 __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_t seed_lo) {
@@ -143,54 +233,100 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// axis = 1 (blocks run along a source row): one wave per output tile; lane l
-// owns row (l & 15), block (l >> 4) of the tile: 64 contiguous bf16 bytes in,
-// 16 code bytes out at tile + 16 l (the wave writes its 1 KB tile in one go).
+// axis = 1 (blocks run along a source row): one wave per output tile (16 rows
+// x 128 K elements). The tile's 4 KB of bf16 is read with each load
+// instruction covering four whole 256-byte row pieces, staged in LDS, and
+// lane l then takes row (l & 15), block (l >> 4): 64 bytes in, 16 code bytes
+// out at tile + 16 l (the wave writes its 1 KB tile in one go). LDS holds
+// row r's 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging
+// writes and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
 // ---------------------------------------------------------------------------
 template <int ROT, int RND>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
     uint32_t seed_hi) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][4096];
+  __shared__ __attribute__((aligned(16))) uint8_t signs_lds[ROT == MX_K_ROT_RAND_SIGN ? 4 : 1][128];
   const int64_t mnp = (rows + 15) & ~(int64_t)15;
   const int64_t nslices = (cols + 127) >> 7;
   const int64_t ntiles = (mnp >> 4) * nslices;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + wv;
   if (tile >= ntiles) return;
   const int lane = threadIdx.x & 63;
   const int64_t g = tile / nslices;
   const int64_t q = tile - g * nslices;
-  const int64_t r = g * 16 + (lane & 15);
-  const int64_t kb = q * 4 + (lane >> 4);
-  const bool valid = r < rows && (kb << 5) < cols;
+  uint8_t *st = stage[wv];
 
-  uint32_t out[4] = {0u, 0u, 0u, 0u};
-  uint32_t s = 0u;                                  // padding: zero codes, scale code 0
-  if (valid) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + r * ld + (kb << 5));
+  // staging: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
+  {
+    const int ch = lane & 15;
+    const int64_t k = q * 128 + ch * 8;                 // first element of the chunk
     u32x4 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src + j);
-    float y[32];
+    for (int j = 0; j < 4; ++j) {
+      const int rr = j * 4 + (lane >> 4);
+      const int64_t r = g * 16 + rr;
+      v[j] = (r < rows && k < cols)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + r * ld + k))
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t d[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        y[8 * j + 2 * t] = bits_f(d[t] << 16);
-        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
-      }
+      const int rr = j * 4 + (lane >> 4);
+      *reinterpret_cast<u32x4 *>(st + rr * 256 + ((ch ^ rr) << 4)) = v[j];
     }
-    if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)(kb << 5), seed_lo);
-    if (ROT != MX_K_ROT_NONE) butterfly32(y);
-    // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
-    const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
-    U4 w{0u, 0u, 0u, 0u};
-    auto u24_of = [&](int i) -> uint32_t {
-      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
-      return pick_word(w, (uint32_t)(i & 3)) >> 8;
-    };
-    s = quantize_block<ROT != MX_K_ROT_NONE, RND>(y, out, u24_of);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int rr = lane & 15, cb = lane >> 4;
+  const int64_t r = g * 16 + rr;
+  const int64_t kb = q * 4 + cb;
+  const bool valid = r < rows && (kb << 5) < cols;
+  float y[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((cb * 4 + j) ^ rr) << 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      y[8 * j + 2 * t] = bits_f(d[t] << 16);
+      y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+    }
+  }
+  if (ROT == MX_K_ROT_RAND_SIGN) {
+    // the tile's 128 reduction indices need 32 Philox calls: lanes 0..31
+    // make one each, the sign bits meet in LDS as one nibble per call
+    uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
+    if (lane < 32) {
+      const U4 sw = sign_words((uint32_t)(q * 32 + lane), seed_lo);
+      sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mask |= sg[cb * 8 + j] << (4 * j);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
+  }
+  if (ROT != MX_K_ROT_NONE) butterfly32(y);
+  // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
+  const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
+  U4 w{0u, 0u, 0u, 0u};
+  auto u24_of = [&](int i) -> uint32_t {
+    if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
+    return pick_word(w, (uint32_t)(i & 3)) >> 8;
+  };
+  uint32_t out[4];
+  uint32_t s = quantize_block<ROT != MX_K_ROT_NONE, RND>(y, out, u24_of);
+  if (!valid) {                                         // padding: zero codes, scale code 0
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = 0u;
+    s = 0u;
   }
   *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
       make_uint4(out[0], out[1], out[2], out[3]);
@@ -269,8 +405,19 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
         const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
         return pick_word(w, (uint32_t)(L & 3)) >> 8;
       };
-      sa = quantize_block<ROT != MX_K_ROT_NONE, RND>(ya, oa, u24_a);
-      if (has_b) sb = quantize_block<ROT != MX_K_ROT_NONE, RND>(yb, ob, u24_b);
+      if (RND == MX_K_ROUND_SR) {
+        quantize_pair_sr<ROT != MX_K_ROT_NONE>(ya, yb, oa, ob, sa, sb,
+                                               (uint64_t)(row0 * cols + c0), cols, seed_lo,
+                                               seed_hi);
+        if (!has_b) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ob[j] = 0u;
+          sb = 0u;
+        }
+      } else {
+        sa = quantize_block<ROT != MX_K_ROT_NONE, RND>(ya, oa, u24_a);
+        if (has_b) sb = quantize_block<ROT != MX_K_ROT_NONE, RND>(yb, ob, u24_b);
+      }
     }
     *reinterpret_cast<uint4 *>(codes + code_offset(c0, kb, nslices)) =
         make_uint4(oa[0], oa[1], oa[2], oa[3]);
