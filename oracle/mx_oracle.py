@@ -27,7 +27,10 @@ What the pages fix, and the readings taken where they are silent:
   * [36Kr] "Fehlerdiagnoseexperiment": stochastic rounding makes the expected
     rounding error zero; the randomized Hadamard flips signs at random before
     the transform; the deterministic Hadamard applies the same orthogonal
-    transform every step, before quantization. Readings: the rotation is the
+    transform every step, before quantization. [36Kr] "Ende-zu-Ende-Effizienz"
+    labels the stabilised run "H16": the variant rotate="hadamard16" applies
+    block-diag(H16, H16) / 4 inside each 32-element block (4 butterfly stages,
+    an exact normalisation). Readings: the default rotation is the
     32-point Sylvester Hadamard H (H_ij = (-1)^popcount(i&j)) scaled by
     c = fp32(1/sqrt(32)), block-diagonal along the GEMM reduction axis and
     aligned with the MX blocks; evaluated in fp32 as a radix-2 butterfly with
@@ -47,6 +50,9 @@ What pins each function (tests/test_oracle_*.py, all "not gpu"):
   sylvester_hadamard    scipy.linalg.hadamard(32); H H^T = 32 I.
   fwht32_f32            exact integer H x for dyadic inputs (explicit matrix
                         product); Parseval; one-hot and constant blocks.
+  fwht16x2_f32          scipy.linalg.hadamard(16); exact integer
+                        block-diag(H16, H16) x / 4 on dyadic inputs; R R x = x;
+                        Parseval; the exact one-hot block.
   philox4x32_10         published Random123 known answers
                         (tests/golden/philox4x32_10_kat.txt) and rocRAND's
                         host engine compiled at test time.
@@ -99,6 +105,8 @@ __all__ = [
     "linear_ref",
     "bf16_round_ref",
     "operand_mse",
+    "fwht16x2_f32",
+    "ROT_HADAMARD16",
 ]
 
 MX_BLOCK = 32          # elements per shared exponent ([36Kr] "Was ist MXFP4?")
@@ -106,6 +114,9 @@ E2M1_EMAX = 2          # largest unbiased exponent of E2M1 (OCP reading)
 HADAMARD_C_F32 = np.float32(1.0 / np.sqrt(np.float64(32)))  # fp32(1/sqrt 32)
 
 ROT_NONE, ROT_HADAMARD, ROT_RAND_SIGN = "none", "hadamard", "rand_sign_hadamard"
+ROT_HADAMARD16 = "hadamard16"
+H16_HALF = 16                 # points per transform of the 16-point variant
+H16_C_F32 = np.float32(0.25)  # 1/sqrt(16), exact in fp32
 ROUND_RNE, ROUND_SR = "rne", "sr"
 
 _M32 = np.uint64(0xFFFFFFFF)
@@ -161,6 +172,28 @@ def fwht32_f32(x: np.ndarray) -> np.ndarray:
         h *= 2
     y = y.reshape(lead + (MX_BLOCK,))
     return (y * HADAMARD_C_F32).astype(np.float32)
+
+
+def fwht16x2_f32(x: np.ndarray) -> np.ndarray:
+    """The 16-point variant: block-diag(H16, H16) / 4 inside each 32-block.
+
+    [36Kr] "Ende-zu-Ende-Effizienz" labels the stabilised run "H16". Each half
+    of a 32-element MX block (elements 0..15 and 16..31) is transformed on its
+    own: butterfly stages with stride h = 1, 2, 4, 8 (lower index fl32(a + b),
+    upper fl32(a - b)), then one multiply by 1/sqrt(16) = 0.25, which is exact.
+    """
+    y = np.array(x, dtype=np.float32, copy=True)
+    lead = y.shape[:-1]
+    assert y.shape[-1] == MX_BLOCK
+    h = 1
+    while h < H16_HALF:
+        y = y.reshape(lead + (MX_BLOCK // (2 * h), 2, h))
+        a = y[..., 0, :]
+        b = y[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2)   # float32 + float32 -> float32
+        h *= 2
+    y = y.reshape(lead + (MX_BLOCK,))
+    return (y * H16_C_F32).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -351,12 +384,15 @@ def quantize_ref(x_bits: np.ndarray, axis: int, block: int = MX_BLOCK,
     if rotate == ROT_RAND_SIGN:
         s = rand_sign_bits(k_index, seed).astype(np.uint32) << np.uint32(31)
         xk = (xk.view(np.uint32) ^ s[None, :]).view(np.float32)
-    elif rotate not in (ROT_NONE, ROT_HADAMARD):
+    elif rotate not in (ROT_NONE, ROT_HADAMARD, ROT_HADAMARD16):
         raise ValueError(rotate)
 
-    # 3. 32-point Hadamard on every block of the reduction axis
+    # 3. 32-point Hadamard (or the 16-point variant) on every block of the
+    #    reduction axis
     blocks = xk.reshape(MN, K // block, block)
-    if rotate != ROT_NONE:
+    if rotate == ROT_HADAMARD16:
+        blocks = fwht16x2_f32(blocks)
+    elif rotate != ROT_NONE:
         blocks = fwht32_f32(blocks)
     y = blocks
 

@@ -97,6 +97,63 @@ def test_fwht_parseval_and_involution():
 
 
 # --------------------------------------------------------------------- Philox
+# ---------------------------------------------------- 16-point variant (H16)
+def test_h16_matches_scipy():
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    H = oracle.sylvester_hadamard(16)
+    assert np.array_equal(H, scipy_linalg.hadamard(16).astype(np.int64))
+    assert np.array_equal(H @ H.T, 16 * np.eye(16, dtype=np.int64))
+
+
+def test_fwht16x2_exact_on_dyadic_inputs():
+    """Small-integer blocks: each half must equal (H16 x_half) / 4 exactly,
+    the two halves independent (block-diag(H16, H16))."""
+    rng = np.random.default_rng(21)
+    H = oracle.sylvester_hadamard(16)
+    x = rng.integers(-1000, 1000, size=(500, 32)).astype(np.int64)
+    exact = np.concatenate([x[:, :16] @ H.T, x[:, 16:] @ H.T], axis=1)
+    want = (exact.astype(np.float32) * np.float32(0.25)).astype(np.float32)
+    got = oracle.fwht16x2_f32(x.astype(np.float32))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # block-diagonal: a one-hot in the first half leaves the second at zero
+    e = np.zeros((1, 32), np.float32)
+    e[0, 3] = 1.0
+    y = oracle.fwht16x2_f32(e)[0]
+    assert np.array_equal(y[:16], 0.25 * H[:, 3].astype(np.float32)) and not y[16:].any()
+
+
+def test_fwht16x2_involution_and_parseval():
+    """R = block-diag(H16, H16) / 4 is orthonormal and its own inverse: on
+    dyadic inputs R R x = x exactly."""
+    rng = np.random.default_rng(22)
+    x = (rng.integers(-500, 500, size=(300, 32)) * 4).astype(np.float32)
+    assert np.array_equal(oracle.fwht16x2_f32(oracle.fwht16x2_f32(x)), x)
+    xb = bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal((2000, 32)).astype(np.float32)))
+    y = oracle.fwht16x2_f32(xb)
+    nx = np.sum(xb.astype(np.float64) ** 2, axis=1)
+    ny = np.sum(y.astype(np.float64) ** 2, axis=1)
+    assert np.max(np.abs(ny - nx) / nx) < 1e-6
+
+
+def test_h16_one_hot_block_is_exact():
+    """x = e_j: its half becomes +-0.25, the other half 0; amax 0.25 gives
+    e = -4 (scale code 123), t = 0.25 * 16 = 4 -> magnitude code 6 on the 16
+    entries of j's half, 0 elsewhere; the dequantized block equals y exactly."""
+    H = oracle.sylvester_hadamard(16)
+    for j in (0, 7, 16, 31):
+        x = np.zeros((1, 32), np.float32)
+        x[0, j] = 1.0
+        q = oracle.quantize_ref(_bf16(x), axis=1, rotate="hadamard16")
+        assert q.scales[0, 0] == 123
+        half = slice(0, 16) if j < 16 else slice(16, 32)
+        other = slice(16, 32) if j < 16 else slice(0, 16)
+        want = np.where(H[:, j % 16] > 0, 6, 14)
+        assert np.array_equal(q.codes[0, half], want)
+        assert not q.codes[0, other].any()
+        d = oracle.dequantize_ref(q.codes, q.scales)[0]
+        assert np.array_equal(d, q.rotated[0].astype(np.float64))
+
+
 def test_philox_published_known_answers():
     for row in _golden_rows("philox4x32_10_kat.txt"):
         v = [int(t, 16) for t in row]
@@ -396,7 +453,7 @@ def test_rotation_cancels_in_product():
     a = f32_to_bf16_bits(rng.standard_normal((40, 128)).astype(np.float32))
     b = f32_to_bf16_bits(rng.standard_normal((24, 128)).astype(np.float32))
     exact = bf16_bits_to_f32(a).astype(np.float64) @ bf16_bits_to_f32(b).astype(np.float64).T
-    for rot, seed in (("hadamard", 0), ("rand_sign_hadamard", 11)):
+    for rot, seed in (("hadamard", 0), ("rand_sign_hadamard", 11), ("hadamard16", 0)):
         qa = oracle.quantize_ref(a, 1, rotate=rot, seed=seed)
         qb = oracle.quantize_ref(b, 1, rotate=rot, seed=seed | (1 << 32))
         rot_prod = qa.rotated.astype(np.float64) @ qb.rotated.astype(np.float64).T
@@ -414,7 +471,8 @@ def test_linear_ops_follow_their_definitions():
     Xf, Wf, dYf = (bf16_bits_to_f32(t).astype(np.float64) for t in (X, W, dY))
     cases = {"fprop": (X, W, Xf @ Wf.T), "dgrad": (dY, W, dYf @ Wf), "wgrad": (dY, X, dYf.T @ Xf)}
     for op, (a, b, exact) in cases.items():
-        for rot, rnd in (("hadamard", "rne"), ("none", "rne"), ("rand_sign_hadamard", "sr")):
+        for rot, rnd in (("hadamard", "rne"), ("none", "rne"), ("rand_sign_hadamard", "sr"),
+                         ("hadamard16", "rne")):
             C, _, _ = oracle.linear_ref(op, a, b, rotate=rot, rounding=rnd, seed=3)
             assert C.shape == exact.shape
             rel = np.linalg.norm(C - exact) / np.linalg.norm(exact)
