@@ -167,7 +167,7 @@ WORKLOADS: Dict[str, Workload] = {
     "fprop_q_proj": Workload(
         "fprop_q_proj", "fprop", 8192, 4096, 4096, 2,
         (("X", 8192, 4096, "act"), ("W", 4096, 4096, "weight")),
-        (DET,), "bf16"),
+        (DET, ("det_hadamard16", "hadamard16", "rne", 0)), "bf16"),
     # Wgrad, gate/up: dY 8192x14336 (1e-4 t_3), X 8192x4096 N(0,1).
     "wgrad_gate_proj": Workload(
         "wgrad_gate_proj", "wgrad", 8192, 14336, 4096, 3,

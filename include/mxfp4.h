@@ -49,11 +49,14 @@ typedef enum mx_status {
 } mx_status;
 
 /* Pre-quantization rotation along the reduction axis (36Kr, section
- * "Fehlerdiagnoseexperiment": randomized vs deterministic Hadamard). */
+ * "Fehlerdiagnoseexperiment": randomized vs deterministic Hadamard; section
+ * "Ende-zu-Ende-Effizienz": the stabilised run is labelled H16). */
 typedef enum mx_rotate {
   MX_ROT_NONE = 0,
   MX_ROT_HADAMARD = 1,            /* y = (H32 x) * fp32(1/sqrt 32), H32 Sylvester */
-  MX_ROT_RAND_SIGN_HADAMARD = 2   /* x_k <- s_k x_k first, s_k = +-1 from Philox */
+  MX_ROT_RAND_SIGN_HADAMARD = 2,  /* x_k <- s_k x_k first, s_k = +-1 from Philox */
+  MX_ROT_HADAMARD16 = 3           /* y = block-diag(H16, H16) x / 4 inside each
+                                     32-element block (two 16-point butterflies) */
 } mx_rotate;
 
 /* Element rounding (36Kr, "Was ist MXFP4?": nearest; "Fehlerdiagnoseexperiment":

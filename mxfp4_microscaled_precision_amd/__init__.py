@@ -29,7 +29,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
-ROTATE = {"none": 0, "hadamard": 1, "rand_sign_hadamard": 2}
+ROTATE = {"none": 0, "hadamard": 1, "rand_sign_hadamard": 2, "hadamard16": 3}
 ROUND = {"rne": 0, "sr": 1}
 OPS = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 OUT_DTYPES = {"f32": 0, "bf16": 1}

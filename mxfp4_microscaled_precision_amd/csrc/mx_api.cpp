@@ -21,7 +21,8 @@ mx_status hip_status(hipError_t e) {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool valid_rotate(int32_t r) {
-  return r == MX_ROT_NONE || r == MX_ROT_HADAMARD || r == MX_ROT_RAND_SIGN_HADAMARD;
+  return r == MX_ROT_NONE || r == MX_ROT_HADAMARD || r == MX_ROT_RAND_SIGN_HADAMARD ||
+         r == MX_ROT_HADAMARD16;
 }
 bool valid_round(int32_t r) { return r == MX_ROUND_RNE || r == MX_ROUND_SR; }
 

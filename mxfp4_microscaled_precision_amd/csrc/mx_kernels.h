@@ -26,7 +26,7 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
   return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shmem, stream);
 }
 
-enum { MX_K_ROT_NONE = 0, MX_K_ROT_HADAMARD = 1, MX_K_ROT_RAND_SIGN = 2 };
+enum { MX_K_ROT_NONE = 0, MX_K_ROT_HADAMARD = 1, MX_K_ROT_RAND_SIGN = 2, MX_K_ROT_HADAMARD16 = 3 };
 enum { MX_K_ROUND_RNE = 0, MX_K_ROUND_SR = 1 };
 
 struct QuantArgs {

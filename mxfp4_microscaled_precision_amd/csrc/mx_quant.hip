@@ -50,8 +50,48 @@ __device__ __forceinline__ void butterfly32(float (&y)[32]) {
   }
 }
 
-// Quantize one 32-element block. v holds the butterfly output h (ROT) or the
-// input x (!ROT). The rotated value is y = fl32(h * c) with c = fp32(1/sqrt 32).
+// The 16-point variant: two independent butterflies (strides 1, 2, 4, 8) on
+// elements 0..15 and 16..31; its normalisation 1/4 is applied like c below.
+__device__ __forceinline__ void butterfly16x2(float (&y)[32]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float a = y[i];
+        const float b = y[i + h];
+        y[i] = __fadd_rn(a, b);
+        y[i + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+}
+
+// Rotation kind of the encoder: 0 none, 1 the 32-point Hadamard (with or
+// without random signs), 2 the 16-point variant.
+template <int ROT>
+struct RotKind {
+  static constexpr int value = ROT == MX_K_ROT_NONE ? 0 : (ROT == MX_K_ROT_HADAMARD16 ? 2 : 1);
+};
+
+template <int ROT>
+__device__ __forceinline__ void rotate_block(float (&y)[32]) {
+  if (ROT == MX_K_ROT_HADAMARD16)
+    butterfly16x2(y);
+  else if (ROT != MX_K_ROT_NONE)
+    butterfly32(y);
+}
+
+// Normalisation of the rotation: fp32(1/sqrt 32), or 1/4 for the 16-point
+// variant.
+template <int RK>
+__device__ __forceinline__ float rot_norm() {
+  return RK == 2 ? 0.25f : bits_f(kInvSqrt32Bits);
+}
+
+// Quantize one 32-element block. v holds the butterfly output h (RK != 0) or
+// the input x (RK == 0). The rotated value is y = fl32(h * c) with c the
+// normalisation (rot_norm).
 //
 //  * amax: max |y| = fl32(max |h| * c), since rounding is monotonic; a NaN
 //    or Inf anywhere in the block marks it (see the amax comment below).
@@ -64,16 +104,17 @@ __device__ __forceinline__ void butterfly32(float (&y)[32]) {
 //    even and saturates at +-6 exactly like the threshold rule (checked over
 //    every fp32 pattern); two elements per instruction, element 2j in the low
 //    nibble. SR: integer rule of e2m1_sr_mag with the Philox uniform.
-template <int ROT, int RND, typename U24Fn>
+template <int RK, int RND, typename U24Fn>
 __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_t (&out)[4],
                                                    U24Fn u24_of) {
   // amax as bits of |v| (a NaN or Inf compares above 0x7f800000). Without
-  // rotation: integer max of |bits|, which sees a lone NaN. With rotation
-  // every output of a block holding a NaN or Inf is itself NaN or Inf, so
-  // the float max of |v| (which skips NaN operands) still lands above
+  // the 32-point rotation: integer max of |bits|, which sees a lone NaN (the
+  // 16-point variant leaves one half finite when the other holds a NaN).
+  // With it every output of a block holding a NaN or Inf is itself NaN or
+  // Inf, so the float max of |v| (which skips NaN operands) still lands above
   // 0x7f800000 for such blocks and equals the integer max for the others.
   uint32_t amax = 0;
-  if (!ROT) {
+  if (RK != 1) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
   } else {
@@ -83,11 +124,11 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
     amax = f_bits(fmaxf(m, fabsf(v[31])));
   }
   const bool nonfinite = amax >= 0x7F800000u;
-  const float c = bits_f(kInvSqrt32Bits);
-  if (ROT) amax = f_bits(__fmul_rn(bits_f(amax), c));
+  const float c = rot_norm<RK>();
+  if (RK) amax = f_bits(__fmul_rn(bits_f(amax), c));
   const int e = block_exponent(amax);
   float t[32];
-  if (!ROT) {
+  if (!RK) {
     const float p = pow2_neg(e);
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], p);
@@ -138,10 +179,10 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
 // 123), else m1 = c, m2 = 2^-e (with rotation); m1 = 2^-e, m2 = 1 without.
 // Returns the scale code (0xFF for a block holding a NaN or Inf, detected as
 // in quantize_block).
-template <int ROT>
+template <int RK>
 __device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1, float &m2) {
   uint32_t amax = 0;
-  if (!ROT) {
+  if (RK != 1) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = max(amax, f_bits(v[i]) & 0x7FFFFFFFu);
   } else {
@@ -151,10 +192,10 @@ __device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1,
     amax = f_bits(fmaxf(m, fabsf(v[31])));
   }
   const bool nonfinite = amax >= 0x7F800000u;
-  const float c = bits_f(kInvSqrt32Bits);
-  if (ROT) amax = f_bits(__fmul_rn(bits_f(amax), c));
+  const float c = rot_norm<RK>();
+  if (RK) amax = f_bits(__fmul_rn(bits_f(amax), c));
   const int e = block_exponent(amax);
-  if (!ROT) {
+  if (!RK) {
     m1 = pow2_neg(e);
     m2 = 1.0f;
   } else {
@@ -167,15 +208,15 @@ __device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1,
 // Stochastic rounding of a column pair (c0, c0 + 1) of the axis-0 path. The
 // elements of row i have source indices L = L0 + i * cols and L + 1, which
 // one Philox call covers unless L % 4 == 3.
-template <int ROT>
+template <int RK>
 __device__ __forceinline__ void quantize_pair_sr(const float (&va)[32], const float (&vb)[32],
                                                  uint32_t (&oa)[4], uint32_t (&ob)[4],
                                                  uint32_t &sa, uint32_t &sb, uint64_t L0,
                                                  int64_t cols, uint32_t seed_lo,
                                                  uint32_t seed_hi) {
   float m1a, m2a, m1b, m2b;
-  sa = block_scale<ROT>(va, m1a, m2a);
-  sb = block_scale<ROT>(vb, m1b, m2b);
+  sa = block_scale<RK>(va, m1a, m2a);
+  sb = block_scale<RK>(vb, m1b, m2b);
 #pragma unroll
   for (int j = 0; j < 4; ++j) oa[j] = ob[j] = 0u;
 #pragma unroll
@@ -313,7 +354,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
   }
-  if (ROT != MX_K_ROT_NONE) butterfly32(y);
+  rotate_block<ROT>(y);
   // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
   const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
   U4 w{0u, 0u, 0u, 0u};
@@ -322,7 +363,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     return pick_word(w, (uint32_t)(i & 3)) >> 8;
   };
   uint32_t out[4];
-  uint32_t s = quantize_block<ROT != MX_K_ROT_NONE, RND>(y, out, u24_of);
+  uint32_t s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
   if (!valid) {                                         // padding: zero codes, scale code 0
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = 0u;
@@ -389,10 +430,8 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
         apply_signs(ya, (uint32_t)(kb << 5), seed_lo);
         apply_signs(yb, (uint32_t)(kb << 5), seed_lo);
       }
-      if (ROT != MX_K_ROT_NONE) {
-        butterfly32(ya);
-        butterfly32(yb);
-      }
+      rotate_block<ROT>(ya);
+      rotate_block<ROT>(yb);
       // stochastic rounding: element (row, c) has L = row * cols + c
       const int64_t row0 = kb << 5;
       auto u24_a = [&](int i) -> uint32_t {
@@ -406,7 +445,7 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
         return pick_word(w, (uint32_t)(L & 3)) >> 8;
       };
       if (RND == MX_K_ROUND_SR) {
-        quantize_pair_sr<ROT != MX_K_ROT_NONE>(ya, yb, oa, ob, sa, sb,
+        quantize_pair_sr<RotKind<ROT>::value>(ya, yb, oa, ob, sa, sb,
                                                (uint64_t)(row0 * cols + c0), cols, seed_lo,
                                                seed_hi);
         if (!has_b) {
@@ -415,8 +454,8 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
           sb = 0u;
         }
       } else {
-        sa = quantize_block<ROT != MX_K_ROT_NONE, RND>(ya, oa, u24_a);
-        if (has_b) sb = quantize_block<ROT != MX_K_ROT_NONE, RND>(yb, ob, u24_b);
+        sa = quantize_block<RotKind<ROT>::value, RND>(ya, oa, u24_a);
+        if (has_b) sb = quantize_block<RotKind<ROT>::value, RND>(yb, ob, u24_b);
       }
     }
     *reinterpret_cast<uint4 *>(codes + code_offset(c0, kb, nslices)) =
@@ -459,6 +498,8 @@ hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream) {
     case 3: return launch_quant<1, 1>(a, stream);
     case 4: return launch_quant<2, 0>(a, stream);
     case 5: return launch_quant<2, 1>(a, stream);
+    case 6: return launch_quant<3, 0>(a, stream);
+    case 7: return launch_quant<3, 1>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

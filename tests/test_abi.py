@@ -67,7 +67,7 @@ def test_quantize_rejects_before_launch():
     P = 4096  # a fake, 16-byte-aligned address; never touched
     assert _q(lib, P, 64, 64, 64, block=16) == -4
     assert _q(lib, P, 64, 64, 64, axis=2) == -4
-    assert _q(lib, P, 64, 64, 64, rot=3) == -4
+    assert _q(lib, P, 64, 64, 64, rot=4) == -4
     assert _q(lib, P, 64, 64, 64, rnd=2) == -4
     assert _q(lib, P, 64, 48, 64, axis=1) == -2          # cols % 32
     assert _q(lib, P, 48, 64, 64, axis=0) == -2          # rows % 32

@@ -14,7 +14,7 @@ from gpu_util import host_u8, rel_fro, to_dev, to_dev_strided
 
 pytestmark = pytest.mark.gpu
 
-ROTS = ("none", "hadamard", "rand_sign_hadamard")
+ROTS = ("none", "hadamard", "rand_sign_hadamard", "hadamard16")
 RNDS = ("rne", "sr")
 GEMM_TOL = 1e-5
 
@@ -69,7 +69,7 @@ def test_quantize_strided_input(mx, axis):
 
 
 @pytest.mark.parametrize("axis", [1, 0])
-@pytest.mark.parametrize("rot", ("none", "hadamard"))
+@pytest.mark.parametrize("rot", ("none", "hadamard", "hadamard16"))
 def test_quantize_every_bf16_pattern(mx, axis, rot):
     """All 65536 bf16 bit patterns (NaN/Inf/subnormal included), plus every
     pattern again with a 7.97 anchor leading each block."""
@@ -164,7 +164,8 @@ def test_gemm_tiny_wgrad_workload(mx):
 
 @pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
 @pytest.mark.parametrize("rot,rnd", [("hadamard", "rne"), ("rand_sign_hadamard", "rne"),
-                                     ("none", "sr"), ("none", "rne")])
+                                     ("none", "sr"), ("none", "rne"), ("hadamard16", "rne"),
+                                     ("hadamard16", "sr")])
 def test_gemm_ops_ragged(mx, op, rot, rnd):
     """T=224, out=96, in=160: every op has M, N off the 128 tile and a K tail."""
     rng = np.random.default_rng(21)
@@ -237,7 +238,8 @@ def test_gemm_deterministic(mx):
 
 
 # --------------------------------------------- full-size workloads, sampled
-FULL = [("fprop_q_proj", "det_hadamard"), ("wgrad_gate_proj", "no_rotation"),
+FULL = [("fprop_q_proj", "det_hadamard"), ("fprop_q_proj", "det_hadamard16"),
+        ("wgrad_gate_proj", "no_rotation"),
         ("wgrad_gate_proj", "det_hadamard"), ("dgrad_down_proj", "det_hadamard"),
         ("dgrad_down_proj", "det_hadamard_sr7")]
 
