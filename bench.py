@@ -33,6 +33,7 @@ PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 GEMM_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm.hip"
+WORKLOADS_REF = None
 GEMM_TRAFFIC = "profiles/gemm_{}_traffic.md"
 QUANT_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_quant.hip"
 QUANT_TRAFFIC = "profiles/quant_{}_traffic.md"
@@ -262,6 +263,8 @@ def main():
 
     import mxfp4_microscaled_precision_amd as mx
     from datagen import WORKLOADS, block_workloads, workload_tensors
+    global WORKLOADS_REF
+    WORKLOADS_REF = WORKLOADS
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -333,6 +336,8 @@ def main():
                       flush=True)
                 del rr
         out["other_workloads"] = extra
+        out["dual_quantizer"] = dual_quant_bench(mx, max(10, args.steps // 2))
+        print(f"[bench] dual quantizer {out['dual_quantizer']}", file=sys.stderr, flush=True)
         wg = WORKLOADS["wgrad_gate_proj"]
         out["wgrad_gate_proj_quant_error"] = output_mse(mx, wg, [v[0] for v in wg.variants])
         print(f"[bench] quant error {out['wgrad_gate_proj_quant_error']}", file=sys.stderr,
@@ -378,6 +383,57 @@ def output_mse(mx, wl, variants):
         res[label] = {"output_mse": float((d * d).mean()),
                       "rel_fro": float(d.norm() / ref.double().norm())}
         del rr, a, b, ref, d, c
+        torch.cuda.empty_cache()
+    return res
+
+
+def dual_quant_bench(mx, steps):
+    """The dual-output quantizer against the two single-orientation launches it
+    replaces, on the Fprop activation X and the Wgrad gradient dY (H32, RNE).
+    Algorithmic bytes: 2 B read + 2 x (0.5 + 1/32) B written per element."""
+    import torch
+    from datagen import workload_tensors
+    res = {}
+    for wname, tname in (("fprop_q_proj", "X"), ("wgrad_gate_proj", "dY")):
+        src = workload_tensors(WORKLOADS_REF[wname])[tname]
+        x = torch.from_numpy(src.view("int16")).view(torch.bfloat16).to("cuda")
+        copies = [x] + [x.clone() for _ in range(max(0, (512 << 20) // (2 * x.numel())))]
+        lib = mx.load_library()
+        st = torch.cuda.current_stream().cuda_stream
+        rows, cols = x.shape
+        outs = {}
+        for axis in (1, 0):
+            cb, sb = mx.quantize_sizes(rows, cols, axis)
+            outs[axis] = (torch.empty(cb, dtype=torch.uint8, device="cuda"),
+                          torch.empty(sb, dtype=torch.uint8, device="cuda"))
+        d1, d0 = mx.QTensorDesc(), mx.QTensorDesc()
+
+        def dual(i):
+            c = copies[i % len(copies)]
+            if lib.mx_quantize_dual(c.data_ptr(), rows, cols, c.stride(0), 32, 1, 0, 0, 0,
+                                    outs[1][0].data_ptr(), outs[1][1].data_ptr(),
+                                    outs[0][0].data_ptr(), outs[0][1].data_ptr(),
+                                    ctypes.byref(d1), ctypes.byref(d0), st):
+                raise RuntimeError("mx_quantize_dual failed")
+
+        def single(axis):
+            def f(i):
+                c = copies[i % len(copies)]
+                if lib.mx_quantize(c.data_ptr(), rows, cols, c.stride(0), axis, 32, 1, 0, 0,
+                                   outs[axis][0].data_ptr(), outs[axis][1].data_ptr(),
+                                   ctypes.byref(d1), st):
+                    raise RuntimeError("mx_quantize failed")
+            return f
+
+        t_d = time_loop(dual, steps, 3) * 1e3
+        t_1 = time_loop(single(1), steps, 3) * 1e3
+        t_0 = time_loop(single(0), steps, 3) * 1e3
+        n = rows * cols
+        res[f"{wname}/{tname} {rows}x{cols}"] = {
+            "dual_us": round(t_d, 2), "axis1_us": round(t_1, 2), "axis0_us": round(t_0, 2),
+            "dual_gbs": round(n * (2 + 2 * (0.5 + 1 / 32)) / (t_d * 1e-6) / 1e9, 1),
+            "speedup_vs_two_launches": round((t_1 + t_0) / t_d, 3)}
+        del copies, outs, x
         torch.cuda.empty_cache()
     return res
 

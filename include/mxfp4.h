@@ -153,6 +153,29 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
                       void *stream);
 
 /*
+ * Both packed orientations of one bf16 tensor from a single read of it: the
+ * axis-1 and the axis-0 operand that mx_quantize would write for this
+ * source, with seeds seed1 and seed0. Each linear layer uses every source
+ * tensor twice, once per orientation (36Kr, section
+ * "Fehlerdiagnoseexperiment": X enters Fprop and Wgrad, W Fprop and Dgrad,
+ * dY Dgrad and Wgrad), so the tensor is read once instead of twice.
+ *
+ *   x_bf16, rows, cols, ld, block, rotate, round : as for mx_quantize, with
+ *       rows % 32 == 0 and cols % 32 == 0 (both are reduction extents here),
+ *       ld % 8 == 0 and x_bf16 16-byte aligned.
+ *   codes1 / scales1 / desc1 : the axis-1 operand (mx_quantize_sizes with
+ *       axis 1 gives the sizes), quantized with seed1.
+ *   codes0 / scales0 / desc0 : the axis-0 operand, quantized with seed0.
+ *   Ownership, alignment of the outputs, the descriptors (may be NULL) and
+ *   the error codes are as for mx_quantize. The results are byte-identical
+ *   to the two mx_quantize calls.
+ */
+mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t block, int32_t rotate, int32_t round, uint64_t seed1,
+                           uint64_t seed0, void *codes1, void *scales1, void *codes0,
+                           void *scales0, mx_qtensor *desc1, mx_qtensor *desc0, void *stream);
+
+/*
  * One GEMM of the triple over two quantized operands, fp32 accumulation on
  * the gfx950 block-scaled FP4 matrix cores:
  *     C[m][n] = sum_k A(m, k) * B(n, k)

@@ -23,7 +23,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "MxError", "QTensorDesc", "QTensor", "load_library", "library_symbols",
-    "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "linear",
+    "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "quantize_dual",
+    "linear",
     "ROTATE", "ROUND", "OPS", "OUT_DTYPES", "OP_AXES",
 ]
 
@@ -74,6 +75,12 @@ _SIGNATURES = {
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
                                    ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.POINTER(QTensorDesc), ctypes.c_void_p]),
+    "mx_quantize_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.POINTER(QTensorDesc),
+                                        ctypes.POINTER(QTensorDesc), ctypes.c_void_p]),
     "mx_linear": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(QTensorDesc),
                                  ctypes.POINTER(QTensorDesc), ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_void_p]),
@@ -216,6 +223,36 @@ def quantize(x, axis: int, rotate: str = "hadamard", round: str = "rne", seed: i
                          ctypes.byref(desc), _stream_handle(x.device, stream))
     _check(st, "mx_quantize")
     return QTensor(codes, scales, desc)
+
+
+def quantize_dual(x, rotate: str = "hadamard", round: str = "rne", seed1: int = 0,
+                  seed0: int = 0, stream=None) -> Tuple[QTensor, QTensor]:
+    """Both orientations of a 2-D bf16 CUDA tensor from one read of it (see
+    mx_quantize_dual): returns (axis-1 operand, axis-0 operand)."""
+    import torch
+    lib = load_library()
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be a CUDA (HIP) tensor; there is no CPU path")
+    if x.numel() > 0 and x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else max(cols, 8 * ((cols + 7) // 8))
+    out = []
+    for axis in (1, 0):
+        cb, sb = quantize_sizes(rows, cols, axis)
+        out.append((torch.empty((cb,), dtype=torch.uint8, device=x.device),
+                    torch.empty((sb,), dtype=torch.uint8, device=x.device)))
+    (c1, s1), (c0, s0) = out
+    d1, d0 = QTensorDesc(), QTensorDesc()
+    ptr = lambda t: t.data_ptr() if t.numel() else None  # noqa: E731
+    st = lib.mx_quantize_dual(ptr(x), rows, cols, ld, 32, ROTATE[rotate], ROUND[round],
+                              seed1 & 0xFFFFFFFFFFFFFFFF, seed0 & 0xFFFFFFFFFFFFFFFF,
+                              ptr(c1), ptr(s1), ptr(c0), ptr(s0), ctypes.byref(d1),
+                              ctypes.byref(d0), _stream_handle(x.device, stream))
+    _check(st, "mx_quantize_dual")
+    return QTensor(c1, s1, d1), QTensor(c0, s0, d0)
 
 
 def linear(op: str, A: QTensor, B: QTensor, out_dtype: str = "f32", out=None,

@@ -140,6 +140,65 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
   return hip_status(mx::quantize_launch(a, static_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t block, int32_t rotate, int32_t round, uint64_t seed1,
+                           uint64_t seed0, void *codes1, void *scales1, void *codes0,
+                           void *scales0, mx_qtensor *desc1, mx_qtensor *desc0, void *stream) {
+  if (block != 32) return MX_ERR_ARG;
+  if (!valid_rotate(rotate) || !valid_round(round)) return MX_ERR_ARG;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  if (rows % 32 != 0 || cols % 32 != 0) return MX_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (x_bf16 == nullptr || codes1 == nullptr || scales1 == nullptr || codes0 == nullptr ||
+        scales0 == nullptr)
+      return MX_ERR_NULL;
+    if (ld < cols) return MX_ERR_SHAPE;
+    if (ld % 8 != 0 || !aligned(x_bf16, 16)) return MX_ERR_ALIGN;
+    if (!aligned(codes1, 16) || !aligned(scales1, 4) || !aligned(codes0, 16) ||
+        !aligned(scales0, 4))
+      return MX_ERR_ALIGN;
+    for (int axis = 0; axis < 2; ++axis) {
+      int64_t mnp, kp;
+      padded_extents(rows, cols, axis, &mnp, &kp);
+      if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
+    }
+  }
+  mx_qtensor *descs[2] = {desc0, desc1};
+  void *cs[2] = {codes0, codes1}, *ss[2] = {scales0, scales1};
+  const uint64_t seeds[2] = {seed0, seed1};
+  for (int axis = 0; axis < 2; ++axis) {
+    if (descs[axis] == nullptr) continue;
+    descs[axis]->codes = cs[axis];
+    descs[axis]->scales = ss[axis];
+    descs[axis]->rows = rows;
+    descs[axis]->cols = cols;
+    descs[axis]->axis = axis;
+    descs[axis]->block = block;
+    descs[axis]->rotate = rotate;
+    descs[axis]->round = round;
+    descs[axis]->seed = seeds[axis];
+  }
+  if (empty) return MX_OK;
+
+  mx::DualArgs a;
+  a.x = static_cast<const uint16_t *>(x_bf16);
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.rotate = rotate;
+  a.round = round;
+  a.seed1_lo = (uint32_t)(seed1 & 0xFFFFFFFFull);
+  a.seed1_hi = (uint32_t)(seed1 >> 32);
+  a.seed0_lo = (uint32_t)(seed0 & 0xFFFFFFFFull);
+  a.seed0_hi = (uint32_t)(seed0 >> 32);
+  a.codes1 = static_cast<uint8_t *>(codes1);
+  a.scales1 = static_cast<uint8_t *>(scales1);
+  a.codes0 = static_cast<uint8_t *>(codes0);
+  a.scales0 = static_cast<uint8_t *>(scales0);
+  return hip_status(mx::quantize_dual_launch(a, static_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C, int64_t ldc,
                     int32_t out_dtype, void *stream) {
   if (op != MX_OP_FPROP && op != MX_OP_DGRAD && op != MX_OP_WGRAD) return MX_ERR_ARG;

@@ -42,6 +42,19 @@ struct QuantArgs {
 
 hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream);
 
+// Both orientations of one source (rows % 32 == 0, cols % 32 == 0).
+struct DualArgs {
+  const uint16_t *x;   // bf16 [rows, cols], leading dimension ld
+  int64_t rows, cols, ld;
+  int rotate, round;
+  uint32_t seed1_lo, seed1_hi;   // axis-1 operand
+  uint32_t seed0_lo, seed0_hi;   // axis-0 operand
+  uint8_t *codes1, *scales1;
+  uint8_t *codes0, *scales0;
+};
+
+hipError_t quantize_dual_launch(const DualArgs &a, hipStream_t stream);
+
 struct GemmArgs {
   const uint8_t *a_codes, *a_scales;  // [M][K/2], [M][K/32]
   const uint8_t *b_codes, *b_scales;  // [N][K/2], [N][K/32]

@@ -467,6 +467,119 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Both orientations from one read. A workgroup stages a 32-row x 128-column
+// piece of the source in LDS (chunk ch of row r at r * 256 + (ch ^ r) * 16,
+// r taken mod 16); threads 0..127 then encode its 128 row blocks into the
+// axis-1 operand (source rows, K along the columns) and threads 128..255 its
+// 128 column blocks into the axis-0 operand (source columns, K along the
+// rows), each exactly as quant_axis1_kernel / quant_axis0_kernel would.
+// Workgroups past the last source row only write the axis-0 operand's K
+// padding (encoded zeros).
+// ---------------------------------------------------------------------------
+template <int ROT, int RND>
+__global__ __launch_bounds__(256) void quant_dual_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t *__restrict__ codes1, uint8_t *__restrict__ scales1, uint32_t s1_lo, uint32_t s1_hi,
+    uint8_t *__restrict__ codes0, uint8_t *__restrict__ scales0, uint32_t s0_lo, uint32_t s0_hi,
+    int64_t gx) {
+  __shared__ __attribute__((aligned(16))) uint8_t st[32 * 256];
+  const int tid = threadIdx.x;
+  const int64_t bx = (int64_t)blockIdx.x % gx, by = (int64_t)blockIdx.x / gx;
+  const int64_t C0 = bx * 128, R0 = by * 32;
+  const int64_t nsl1 = (cols + 127) >> 7;   // axis-1 operand: MN = rows, K = cols
+  const int64_t nsl0 = (rows + 127) >> 7;   // axis-0 operand: MN = cols, K = rows
+  const bool rows_live = R0 < rows;
+
+  if (rows_live) {
+    const int ch = tid & 15;
+    const int64_t c = C0 + ch * 8;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = (tid >> 4) + 16 * j;
+      const u32x4 v = c < cols ? __builtin_nontemporal_load(
+                                     reinterpret_cast<const u32x4 *>(x + (R0 + rr) * ld + c))
+                               : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(st + rr * 256 + ((ch ^ (rr & 15)) << 4)) = v;
+    }
+  }
+  __syncthreads();
+
+  float y[32];
+  uint32_t out[4];
+  uint32_t s;
+  if (tid < 128) {
+    if (!rows_live) return;
+    // axis 1: row R0 + rr, 32-block kb along the columns
+    const int rr = tid & 31, b = tid >> 5;
+    const int64_t r = R0 + rr;
+    const int64_t kb = (C0 >> 5) + b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((b * 4 + j) ^ (rr & 15)) << 4));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        y[8 * j + 2 * t] = bits_f(d[t] << 16);
+        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+      }
+    }
+    if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)(kb << 5), s1_lo);
+    rotate_block<ROT>(y);
+    const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;   // L % 4 == 0
+    U4 w{0u, 0u, 0u, 0u};
+    auto u24_of = [&](int i) -> uint32_t {
+      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), s1_lo, s1_hi);
+      return pick_word(w, (uint32_t)(i & 3)) >> 8;
+    };
+    s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
+    if ((kb << 5) >= cols) {                              // K padding of the operand
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = 0u;
+      s = 0u;
+    }
+    *reinterpret_cast<uint4 *>(codes1 + code_offset(r, kb, nsl1)) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    scales1[scale_offset(r, kb, rows)] = (uint8_t)s;
+  } else {
+    // axis 0: column C0 + cc, 32-block R0 / 32 along the rows
+    const int cc = tid - 128;
+    const int64_t c = C0 + cc;
+    if (c >= cols) return;
+    const int64_t kb = R0 >> 5;
+    if (rows_live) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint16_t bits =
+            *reinterpret_cast<const uint16_t *>(st + j * 256 + (((cc >> 3) ^ (j & 15)) << 4) + (cc & 7) * 2);
+        y[j] = bits_f((uint32_t)bits << 16);
+      }
+      if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)R0, s0_lo);
+      rotate_block<ROT>(y);
+      auto u24_of = [&](int i) -> uint32_t {
+        const uint64_t L = (uint64_t)((R0 + i) * cols + c);
+        return pick_word(sr_words(L >> 2, s0_lo, s0_hi), (uint32_t)(L & 3)) >> 8;
+      };
+      s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
+    } else {                                              // K padding of the operand
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = 0u;
+      s = 0u;
+    }
+    *reinterpret_cast<uint4 *>(codes0 + code_offset(c, kb, nsl0)) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    scales0[scale_offset(c, kb, cols)] = (uint8_t)s;
+  }
+}
+
+template <int ROT, int RND>
+hipError_t launch_dual(const DualArgs &a, hipStream_t stream) {
+  const int64_t gx = (a.cols + 127) / 128;
+  const int64_t gy = ((a.rows + 127) >> 7) * 4;          // K blocks of the axis-0 operand
+  return launch(quant_dual_kernel<ROT, RND>, dim3((unsigned)(gx * gy)), dim3(256), 0, stream,
+                a.x, a.rows, a.cols, a.ld, a.codes1, a.scales1, a.seed1_lo, a.seed1_hi,
+                a.codes0, a.scales0, a.seed0_lo, a.seed0_hi, gx);
+}
+
 template <int ROT, int RND>
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
@@ -489,6 +602,20 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t quantize_dual_launch(const DualArgs &a, hipStream_t stream) {
+  switch (a.rotate * 2 + a.round) {
+    case 0: return launch_dual<0, 0>(a, stream);
+    case 1: return launch_dual<0, 1>(a, stream);
+    case 2: return launch_dual<1, 0>(a, stream);
+    case 3: return launch_dual<1, 1>(a, stream);
+    case 4: return launch_dual<2, 0>(a, stream);
+    case 5: return launch_dual<2, 1>(a, stream);
+    case 6: return launch_dual<3, 0>(a, stream);
+    case 7: return launch_dual<3, 1>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream) {
   switch (a.rotate * 2 + a.round) {

@@ -104,6 +104,44 @@ def _lin(lib, op, A, B, C=4096, ldc=None, out=0):
     return lib.mx_linear(op, ctypes.byref(A), ctypes.byref(B), C, ldc, out, None)
 
 
+def _qd(lib, x, rows, cols, ld, block=32, rot=1, rnd=0, c1=None, s1=None, c0=None, s0=None):
+    P = 4096
+    d1, d0 = mx.QTensorDesc(), mx.QTensorDesc()
+    return lib.mx_quantize_dual(x, rows, cols, ld, block, rot, rnd, 0, 0,
+                                P if c1 is None else c1, P if s1 is None else s1,
+                                P if c0 is None else c0, P if s0 is None else s0,
+                                ctypes.byref(d1), ctypes.byref(d0), None)
+
+
+def test_quantize_dual_rejects_before_launch():
+    """Validation of mx_quantize_dual fails before any HIP call."""
+    lib = mx.load_library()
+    P = 4096
+    assert _qd(lib, P, 64, 64, 64, block=16) == -4
+    assert _qd(lib, P, 64, 64, 64, rot=4) == -4
+    assert _qd(lib, P, 64, 64, 64, rnd=2) == -4
+    assert _qd(lib, P, 64, 48, 64) == -2                 # cols % 32
+    assert _qd(lib, P, 48, 64, 64) == -2                 # rows % 32
+    assert _qd(lib, P, 64, 64, 32) == -2                 # ld < cols
+    assert _qd(lib, P, 64, 64, 68) == -3                 # ld % 8
+    assert _qd(lib, P + 2, 64, 64, 64) == -3             # x misaligned
+    assert _qd(lib, P, 64, 64, 64, c0=P + 4) == -3       # axis-0 codes misaligned
+    assert _qd(lib, P, 64, 64, 64, s1=P + 2) == -3       # axis-1 scales misaligned
+    assert _qd(lib, None, 64, 64, 64) == -1
+    assert _qd(lib, P, 64, 64, 64, c1=0) == -1
+    assert _qd(lib, P, 1 << 17, 1 << 14, 1 << 14) == -6  # codes of 1 GiB
+
+
+def test_quantize_dual_empty_fills_both_descriptors():
+    lib = mx.load_library()
+    d1, d0 = mx.QTensorDesc(), mx.QTensorDesc()
+    st = lib.mx_quantize_dual(None, 0, 64, 64, 32, 3, 1, 5, 6, None, None, None, None,
+                              ctypes.byref(d1), ctypes.byref(d0), None)
+    assert st == 0
+    assert (d1.axis, d1.rotate, d1.round, d1.seed, d1.cols) == (1, 3, 1, 5, 64)
+    assert (d0.axis, d0.rotate, d0.round, d0.seed, d0.cols) == (0, 3, 1, 6, 64)
+
+
 def test_linear_rejects_before_launch():
     lib = mx.load_library()
     X, W = _desc(64, 128, 1), _desc(96, 128, 1)

@@ -132,6 +132,50 @@ def test_quantize_empty(mx):
     assert q.codes.numel() == 0 and q.scales.numel() == 0
 
 
+# ------------------------------------------------------------ dual output
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 160), (320, 384), (160, 256)])
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_dual_matches_oracle_and_single(mx, shape, rot, rnd):
+    """Both outputs equal the oracle's axis-1 and axis-0 quantizations (tiled,
+    padding included) and the two single-axis launches, byte for byte."""
+    rng = np.random.default_rng(shape[0] * 13 + shape[1])
+    x = _rand_bits(rng, shape)
+    xd = to_dev(x)
+    q1, q0 = mx.quantize_dual(xd, rot, rnd, seed1=21, seed0=22 | (1 << 32))
+    s1 = mx.quantize(xd, 1, rot, rnd, seed=21)
+    s0 = mx.quantize(xd, 0, rot, rnd, seed=22 | (1 << 32))
+    _sync()
+    _check_q(q1, oracle.quantize_ref(x, 1, rotate=rot, rounding=rnd, seed=21), f"dual axis 1 {shape}")
+    _check_q(q0, oracle.quantize_ref(x, 0, rotate=rot, rounding=rnd, seed=22 | (1 << 32)),
+             f"dual axis 0 {shape}")
+    for a, b in ((q1, s1), (q0, s0)):
+        assert np.array_equal(host_u8(a.codes), host_u8(b.codes))
+        assert np.array_equal(host_u8(a.scales), host_u8(b.scales))
+
+
+def test_quantize_dual_strided_and_full_size(mx):
+    """A row-strided source, and the full-size Fprop activation (8192 x 4096)
+    against the single-axis launches."""
+    import torch
+    rng = np.random.default_rng(77)
+    x = _rand_bits(rng, (128, 192))
+    big = torch.zeros((128, 200), dtype=torch.bfloat16, device="cuda")
+    big[:, :192] = to_dev(x)
+    q1, q0 = mx.quantize_dual(big[:, :192], "hadamard", "rne")
+    _sync()
+    _check_q(q1, oracle.quantize_ref(x, 1), "strided dual axis 1")
+    _check_q(q0, oracle.quantize_ref(x, 0), "strided dual axis 0")
+    w = WORKLOADS["fprop_q_proj"]
+    X = to_dev(workload_tensors(w)["X"])
+    q1, q0 = mx.quantize_dual(X, "hadamard", "rne", seed1=0, seed0=0)
+    s1 = mx.quantize(X, 1)
+    s0 = mx.quantize(X, 0)
+    _sync()
+    for a, b in ((q1, s1), (q0, s0)):
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
 # ----------------------------------------------------------------------- GEMM
 def _gemm_case(mx, op, a_src, b_src, rot, rnd, seed, check_bf16=True):
     ax_a, ax_b = mx.OP_AXES[op]
