@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload/variant and the full block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--structural", action="store_true",
+                    help="also run the repeated-Wgrad structural-error harness")
     ap.add_argument("--cpu-reps", type=int, default=3,
                     help="repetitions of the whole-workload oracle run (cpu_baseline)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -343,6 +345,9 @@ def main():
         print(f"[bench] quant error {out['wgrad_gate_proj_quant_error']}", file=sys.stderr,
               flush=True)
         out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 5))
+    if args.structural or args.all:
+        out["structural_error"] = structural_error(mx)
+        print("[bench] structural error done", file=sys.stderr, flush=True)
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -436,6 +441,60 @@ def dual_quant_bench(mx, steps):
         del copies, outs, x
         torch.cuda.empty_cache()
     return res
+
+
+STRUCTURAL_VARIANTS = (("det_hadamard", "hadamard", "rne", False),
+                       ("det_hadamard16", "hadamard16", "rne", False),
+                       ("rand_sign_hadamard", "rand_sign_hadamard", "rne", True),
+                       ("no_rotation_sr", "none", "sr", True),
+                       ("hadamard_sr", "hadamard", "sr", True))
+
+
+def structural_error(mx, T=8192, n_out=2048, n_in=1024, steps=64, data_seed=3):
+    """Error of Wgrad repeated over `steps` steps on fixed tensors.
+
+    dY [T, n_out] = 1e-4 t_3 and X [T, n_in] ~ N(0, 1) (bf16, the Wgrad
+    gate/up distributions) stay fixed; step k computes dW_k = dY^T X through
+    the MXFP4 path (both operands quantized along T), with seed k for the
+    randomized variants (random signs, stochastic rounding) and the same
+    deterministic rotation every step otherwise. For K = 1, 2, 4, ... the
+    relative Frobenius error of the K-step mean against the fp32 product of
+    the bf16 operands is reported, with the single-step error: a fixed error
+    pattern keeps the mean's error at the single-step value, a pattern that
+    changes from step to step lets it fall. The reference product is a plain
+    torch fp32 matmul (measurement only)."""
+    import numpy as np
+    import torch
+    from datagen import normal_bf16, student_t_bf16
+    rng = np.random.Generator(np.random.PCG64(data_seed))
+    dY = student_t_bf16(rng, (T, n_out), 3.0, 1e-4)
+    X = normal_bf16(rng, (T, n_in), 1.0)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to("cuda")  # noqa: E731
+    dYd, Xd = dev(dY), dev(X)
+    ref = torch.matmul(dYd.float().t().contiguous(), Xd.float())
+    ref_norm = ref.double().norm().item()
+    out = {"shape": {"T": T, "out": n_out, "in": n_in}, "steps": steps, "variants": {}}
+    Ks = [k for k in (1, 2, 4, 8, 16, 32, 64, 128, 256) if k <= steps]
+    for label, rot, rnd, reseed in STRUCTURAL_VARIANTS:
+        acc = torch.zeros_like(ref, dtype=torch.float64)
+        single = []
+        curve = {}
+        for k in range(1, steps + 1):
+            seed = k if reseed else 0
+            qa = mx.quantize(dYd, 0, rot, rnd, seed=seed)
+            qb = mx.quantize(Xd, 0, rot, rnd, seed=seed | (1 << 32))
+            c = mx.linear("wgrad", qa, qb, "f32")
+            acc += c.double()
+            if k <= 4:
+                single.append(((c.double() - ref.double()).norm() / ref_norm).item())
+            if k in Ks:
+                curve[k] = ((acc / k - ref.double()).norm() / ref_norm).item()
+        out["variants"][label] = {
+            "rotate": rot, "round": rnd, "new_seed_per_step": reseed,
+            "single_step_rel_err": [round(v, 6) for v in single],
+            "mean_rel_err": {str(k): round(v, 6) for k, v in curve.items()},
+            "mean_over_single": round(curve[Ks[-1]] / single[0], 4)}
+    return out
 
 
 def bench_block(mx, wls, steps):

@@ -333,3 +333,20 @@ def test_full_size_sampled(mx, name, variant):
         _sync()
         got_b = cb.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
         assert np.array_equal(got_b, oracle.bf16_round_ref(c_host))
+
+
+# ------------------------------------------------- structural-error harness
+def test_structural_error_harness_separates_fixed_and_changing_errors(mx):
+    """The repeated-Wgrad harness on a small problem: with a deterministic
+    rotation every step reproduces the same dW bit for bit, so the error of
+    the K-step mean equals the single-step error; with a new seed per step
+    (random signs, stochastic rounding) the mean's error falls below it."""
+    import bench
+    res = bench.structural_error(mx, T=1024, n_out=256, n_in=128, steps=16)
+    v = res["variants"]
+    for det in ("det_hadamard", "det_hadamard16"):
+        s = v[det]["single_step_rel_err"]
+        assert len(set(s)) == 1, det
+        assert abs(v[det]["mean_rel_err"]["16"] - s[0]) <= 1e-6 * s[0], det
+    for rnd in ("rand_sign_hadamard", "no_rotation_sr", "hadamard_sr"):
+        assert v[rnd]["mean_rel_err"]["16"] < 0.7 * v[rnd]["single_step_rel_err"][0], rnd
