@@ -96,17 +96,19 @@ __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_ba
 }
 
 // ---------------------------------------------------------------------------
-// 256x256 block tile, eight waves (two per SIMD) in a 2x4 grid, 128x64 per
-// wave = 8x4 MFMA tiles (128 fp32 accumulators per lane); two waves per SIMD
-// let one wave's MFMAs cover the other's stalls.
+// 256x256 block tile. Twelve waves, three per SIMD: eight consumer waves in
+// a 2x4 grid, 128x64 each = 8x4 MFMA tiles (128 fp32 accumulators per lane),
+// and four producer waves that only copy. A direct-to-LDS copy can hold its
+// wave at issue for hundreds of cycles while the L1 waits on pending L2
+// reads; on a wave that also issues MFMAs that stall idles the matrix core,
+// on a producer it costs nothing.
 //
 // Operands are in the tiled layout the quantizer writes: a 1 KB tile holds 16
 // rows x 128 K elements as [32-block c][row r][16 B], which is exactly the
 // 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; scales of a
 // 128-wide K slice are one contiguous run of 4 bytes per row. K advances one
 // slice per stage through a ring of four LDS stage buffers with three stages
-// in flight; each stage's copies are spread over its MFMA rows and the next
-// stage's fragments are read while the current one's MFMAs run. Every copy is a direct-to-LDS load of one contiguous span (a
+// in flight. Every copy is a direct-to-LDS load of one contiguous span (a
 // 1 KB tile or 256 bytes of scales), and every LDS fragment read is one
 // contiguous 1 KB span, the only pattern gfx950's LDS serves at its full 256
 // bytes per clock (measured: a row-major layout takes 4x and an XOR-swizzled
@@ -116,7 +118,8 @@ __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_ba
 // ---------------------------------------------------------------------------
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kThreads = 512;
+constexpr int kThreads = 768;                      // 8 consumer + 4 producer waves
+constexpr int kConsumers = 8;
 constexpr int kStageA = kBM * 64;                  // 16 tiles of 1 KB
 constexpr int kStageB = kBN * 64;
 constexpr int kStageSA = kBM * 4;                  // 1 KB of scales
@@ -150,60 +153,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7
-  const int wm = wave >> 2, wn = wave & 3;                     // 2 x 4 wave grid
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..11
+  const bool producer = wave >= kConsumers;
+  const int wm = (wave >> 2) & 1, wn = wave & 3;               // consumers: 2 x 4 grid
   const int64_t tm = (g.M + kBM - 1) / kBM, tn = (g.N + kBN - 1) / kBN;
   int64_t mi, ni;
   tile_coords(blockIdx.x, tm, tn, &mi, &ni);
   const int m0 = (int)(mi * kBM), n0 = (int)(ni * kBN);
   const int mp = (int)((g.M + 15) & ~15LL), np = (int)((g.N + 15) & ~15LL);   // padded rows
   const int nslices = (int)((g.K + 127) >> 7);
-  const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
-  const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
-  const v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
-  const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
-  const v4i rsrc_s = wave < 4 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
-                              : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
-
-  // Codes: wave w copies row groups 2w, 2w + 1 of the block's A and B rows;
-  // group G, slice s is the 1 KB at (G * nslices + s) * 1 KB. Groups past the
-  // padded extent (wave-uniform test) load from the buffer end, i.e. zeros.
-  const int ga = (m0 >> 4) + wave * 2, gb = (n0 >> 4) + wave * 2;
-  const int a_lane = ga * nslices * 1024 + lane * 16;
-  const int b_lane = gb * nslices * 1024 + lane * 16;
-  // Scales: waves 0..3 copy A's rows 64 w .. 64 w + 63, waves 4..7 B's;
-  // rows past the padded extent load zeros.
-  const int s_rows = wave < 4 ? mp : np;
-  const int s_row = (wave < 4 ? m0 : n0) + (wave & 3) * 64 + lane;
-  const int s_bytes = wave < 4 ? sa_bytes : sb_bytes;
-  const int s_lane = s_row * 4;
-  const uint32_t s_lds = (uint32_t)(kStageA + kStageB + (wave < 4 ? 0 : kStageSA) + (wave & 3) * 256);
-
-  // DMA instruction `part` (0, 1: A tiles; 2, 3: B tiles; 4: scales) of
-  // stage s into ring buffer buf. Stages past the last slice read zeros, so
-  // every stage issues the same five instructions and the vmcnt bookkeeping
-  // stays uniform.
-  auto issue_part = [&](int s, int buf, int part) {
-    const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
-    const bool live = s < nslices;
-    if (part < 4) {
-      const int j = part & 1;
-      const bool is_b = part >= 2;
-      int l = is_b ? b_lane : a_lane;
-      asm volatile("" : "+v"(l));
-      const int off = (j * nslices + s) * 1024;
-      const bool ok = live && ((is_b ? gb : ga) + j) * 16 < (is_b ? np : mp);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          stage + (uint32_t)((wave * 2 + j) * 1024 + (is_b ? kStageA : 0)));
-      dma_load16(is_b ? rsrc_b : rsrc_a, ok ? l + off : (is_b ? b_bytes : a_bytes), dst);
-    } else {
-      int l = s_lane;
-      asm volatile("" : "+v"(l));
-      dma_load4(rsrc_s, (live && s_row < s_rows) ? l + s * s_rows * 4 : s_bytes,
-                __builtin_amdgcn_readfirstlane(stage + s_lds));
-    }
-  };
+  const int lr = lane & 15;      // row within a 16-row MFMA tile
+  const int lg = lane >> 4;      // 32-element K block within the slice
 
   v4f acc[8][4];
 #pragma unroll
@@ -211,87 +172,79 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int lr = lane & 15;      // row within a 16-row MFMA tile
-  const int lg = lane >> 4;      // 32-element K block within the slice
-  const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
-  const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
-  const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
-  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
-  auto ld16 = [&](int buf, uint32_t off) {
-    return *reinterpret_cast<const uint4 *>(smem + buf * kStageBytes + off);
-  };
-  // the MFMA reads byte 0 of its scale operand: shift K block lg's byte there
-  auto ld_scale = [&](int buf, uint32_t off) {
-    return *reinterpret_cast<const uint32_t *>(smem + buf * kStageBytes + off) >> (8 * lg);
-  };
-
-  for (int p = 0; p < kAhead; ++p)
+  if (producer) {
+    // Producer p copies row groups 4p .. 4p + 3 of A and of B and scale rows
+    // 64p .. 64p + 63 of A and of B: ten DMA instructions per stage. Stages
+    // past the last slice read zeros so the counts stay uniform.
+    const int p = wave - kConsumers;
+    const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
+    const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
+    const v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
+    const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
+    const v4i rsrc_sa = make_rsrc(g.a_scales, (uint32_t)sa_bytes);
+    const v4i rsrc_sb = make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+    const int ga = (m0 >> 4) + p * 4, gb = (n0 >> 4) + p * 4;
+    const int a_lane = ga * nslices * 1024 + lane * 16;
+    const int b_lane = gb * nslices * 1024 + lane * 16;
+    const int sa_row = m0 + p * 64 + lane, sb_row = n0 + p * 64 + lane;
+    auto issue = [&](int s, int buf) {
+      const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
+      const bool live = s < nslices;
+      int al = a_lane, bl = b_lane, sal = sa_row * 4, sbl = sb_row * 4;
+      asm volatile("" : "+v"(al), "+v"(bl), "+v"(sal), "+v"(sbl));
 #pragma unroll
-    for (int part = 0; part < 5; ++part) issue_part(p, p, part);
-  asm volatile("s_waitcnt vmcnt(10)" ::: "memory");   // this wave's part of stage 0
-  __syncthreads();
-
-  uint4 bf[4], bn[4], a0, a1;
-  uint32_t sb[4], sbn[4], sa[8], san[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf[j] = ld16(0, b_off + j * 1024);
-    sb[j] = ld_scale(0, sb_off + j * 64);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sa[i] = ld_scale(0, sa_off + i * 64);
-  a0 = ld16(0, a_off);
-  a1 = ld16(0, a_off + 1024);
-
-  // Stage s: 8 rows of 4 MFMAs. A fragments stream two rows ahead. After
-  // row 3 the wave waits for its part of stage s + 1, and the barrier makes
-  // every wave's part visible and frees the buffer of stage s - 1, which
-  // rows 3..7 then refill with stage s + 3 (one DMA instruction per row).
-  // Rows 4..7 also read stage s + 1's B fragments, scales and first two A
-  // rows, so the next stage starts without an LDS round trip.
-  for (int s = 0; s < nslices; ++s) {
-    const int cur = s & 3, nxt = (s + 1) & 3, refill = (s + 3) & 3;
-    uint4 af[8];
-    af[0] = a0;
-    af[1] = a1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i + 2 < 8) af[i + 2] = ld16(cur, a_off + (i + 2) * 1024);
-      if (i == 4) {
-        bn[0] = ld16(nxt, b_off);
-        bn[1] = ld16(nxt, b_off + 1024);
-        sbn[0] = ld_scale(nxt, sb_off);
-        sbn[1] = ld_scale(nxt, sb_off + 64);
-      } else if (i == 5) {
-        bn[2] = ld16(nxt, b_off + 2048);
-        bn[3] = ld16(nxt, b_off + 3072);
-        sbn[2] = ld_scale(nxt, sb_off + 128);
-        sbn[3] = ld_scale(nxt, sb_off + 192);
-      } else if (i == 6) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) san[r] = ld_scale(nxt, sa_off + r * 64);
-        a0 = ld16(nxt, a_off);
-      } else if (i == 7) {
-        a1 = ld16(nxt, a_off + 1024);
+      for (int j = 0; j < 4; ++j) {
+        const int off = (j * nslices + s) * 1024;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 4 + j) * 1024));
+        dma_load16(rsrc_a, (live && (ga + j) * 16 < mp) ? al + off : a_bytes, dst);
+        dma_load16(rsrc_b, (live && (gb + j) * 16 < np) ? bl + off : b_bytes, dst + kStageA);
       }
+      dma_load4(rsrc_sa, (live && sa_row < mp) ? sal + s * mp * 4 : sa_bytes,
+                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kStageA + kStageB + p * 256)));
+      dma_load4(rsrc_sb, (live && sb_row < np) ? sbl + s * np * 4 : sb_bytes,
+                __builtin_amdgcn_readfirstlane(
+                    stage + (uint32_t)(kStageA + kStageB + kStageSA + p * 256)));
+    };
+    for (int s = 0; s < kAhead; ++s) issue(s, s);
+    for (int s = 0; s < nslices; ++s) {
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // own part of stage s landed
+      __syncthreads();                                     // stage s visible; s - 1 free
+      issue(s + kAhead, (s + kAhead) & 3);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // zero-fill loads past the end
+  } else {
+    const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
+    const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
+    const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
+    const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
+    for (int s = 0; s < nslices; ++s) {
+      __syncthreads();                                     // stage s landed
+      const uint8_t *base = smem + (s & 3) * kStageBytes;
+      uint4 bf[4];
+      uint32_t sb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af[i], acc[i][j], sb[j], sa[i]);
-      if (i == 3) {
-        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");   // own part of stage s + 1
-        __syncthreads();
+      for (int j = 0; j < 4; ++j) {
+        bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
+        sb[j] = *reinterpret_cast<const uint32_t *>(base + sb_off + j * 64) >> (8 * lg);
       }
-      if (i >= 3) issue_part(s + kAhead, refill, i - 3);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      uint4 af = *reinterpret_cast<const uint4 *>(base + a_off);
+      uint32_t sa = *reinterpret_cast<const uint32_t *>(base + sa_off) >> (8 * lg);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[j] = bn[j];
-      sb[j] = sbn[j];
-    }
+      for (int i = 0; i < 8; ++i) {
+        uint4 af_next = af;
+        uint32_t sa_next = sa;
+        if (i + 1 < 8) {
+          af_next = *reinterpret_cast<const uint4 *>(base + a_off + (i + 1) * 1024);
+          sa_next = *reinterpret_cast<const uint32_t *>(base + sa_off + (i + 1) * 64) >> (8 * lg);
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sa[i] = san[i];
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af, acc[i][j], sb[j], sa);
+        af = af_next;
+        sa = sa_next;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // zero-fill loads past the end
 
   // Epilogue. Fast path (N and ldc multiples of 8, C 16-byte aligned): the tile goes through the now idle LDS
   // ring in row-major order and leaves as whole 512-byte (bf16) or 1 KB
@@ -310,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
     for (int h = 0; h < 256 / kRowsPerPass; ++h) {
       __syncthreads();                               // ring (or previous pass) no longer read
-      if (OUT_BF16 || wm == h) {
+      if (!producer && (OUT_BF16 || wm == h)) {
         const int rbase = OUT_BF16 ? wm * 128 : 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -343,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
         }
       }
     }
-  } else {
+  } else if (!producer) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
