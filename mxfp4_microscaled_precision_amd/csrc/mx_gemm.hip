@@ -19,6 +19,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "mx_kernels.h"
 
 namespace mx {
@@ -133,20 +136,45 @@ constexpr int kGroupM = 8;                         // tile rows per ordering gro
 // the 8 XCDs, so consecutive ids are first regrouped per XCD, then ordered in
 // groups of kGroupM tile rows so that each XCD works on a compact 2-D region
 // of C and shares its A and B panels through its own L2.
-__device__ __forceinline__ void tile_coords(int64_t bid, int64_t tm, int64_t tn, int64_t *mi,
-                                            int64_t *ni) {
-  const int64_t T = tm * tn;
-  int64_t id = bid;
+__device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int *mi, int *ni) {
+  const int T = tm * tn;
+  int id = bid;
   if ((T & 7) == 0) id = (bid & 7) * (T >> 3) + (bid >> 3);
-  const int64_t per_group = kGroupM * tn;
-  const int64_t grp = id / per_group;
-  const int64_t first_m = grp * kGroupM;
-  const int64_t gm = min((int64_t)kGroupM, tm - first_m);
-  const int64_t r = id - grp * per_group;
+  const int per_group = kGroupM * tn;
+  const int grp = id / per_group;
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, tm - first_m);
+  const int r = id - grp * per_group;
   *mi = first_m + r % gm;
   *ni = r / gm;
 }
 
+// One finished quad: lane (lr, lg) of a 16x16 tile holds C[row][col .. col + 3]
+// (B is the MFMA's first operand). One 8-byte (bf16) or 16-byte (fp32)
+// store when the address allows it, else element-wise.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc, int64_t row,
+                                               int64_t col, bool vec_ok) {
+  if (row >= g.M) return;
+  if (vec_ok && col + 3 < g.N) {
+    if (OUT_BF16) {
+      uint2 v;
+      v.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+      v.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col) = v;
+    } else {
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  } else {
+    store_quad<OUT_BF16>(g, acc, row, col);
+  }
+}
+
+// Persistent: one workgroup per compute unit walks the tiles bid, bid + grid,
+// ... as one continuous sequence of stages; producers run three stages ahead
+// across tile boundaries, and consumers store a finished tile while the next
+// tile's first stages are already in flight.
 template <int OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes];
@@ -156,26 +184,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..11
   const bool producer = wave >= kConsumers;
   const int wm = (wave >> 2) & 1, wn = wave & 3;               // consumers: 2 x 4 grid
-  const int64_t tm = (g.M + kBM - 1) / kBM, tn = (g.N + kBN - 1) / kBN;
-  int64_t mi, ni;
-  tile_coords(blockIdx.x, tm, tn, &mi, &ni);
-  const int m0 = (int)(mi * kBM), n0 = (int)(ni * kBN);
+  const int tm = (int)((g.M + kBM - 1) / kBM), tn = (int)((g.N + kBN - 1) / kBN);
+  const int tiles = tm * tn;
+  const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int ntl = (tiles - bid + grid - 1) / grid;             // tiles of this workgroup
   const int mp = (int)((g.M + 15) & ~15LL), np = (int)((g.N + 15) & ~15LL);   // padded rows
   const int nslices = (int)((g.K + 127) >> 7);
+  const int total = ntl * nslices;                             // stages of this workgroup
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
   const int lr = lane & 15;      // row within a 16-row MFMA tile
   const int lg = lane >> 4;      // 32-element K block within the slice
 
-  v4f acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
   if (producer) {
     // Producer p copies row groups 4p .. 4p + 3 of A and of B and scale rows
     // 64p .. 64p + 63 of A and of B: ten DMA instructions per stage. Stages
-    // past the last slice read zeros so the counts stay uniform.
+    // past the last one read zeros so the counts stay uniform.
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
@@ -183,126 +206,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
     const v4i rsrc_sa = make_rsrc(g.a_scales, (uint32_t)sa_bytes);
     const v4i rsrc_sb = make_rsrc(g.b_scales, (uint32_t)sb_bytes);
-    const int ga = (m0 >> 4) + p * 4, gb = (n0 >> 4) + p * 4;
-    const int a_lane = ga * nslices * 1024 + lane * 16;
-    const int b_lane = gb * nslices * 1024 + lane * 16;
-    const int sa_row = m0 + p * 64 + lane, sb_row = n0 + p * 64 + lane;
-    auto issue = [&](int s, int buf) {
+    int ga = 0, gb = 0, sa_row = 0, sb_row = 0;
+    bool tile_live = false;
+    auto set_tile = [&](int k) {
+      tile_live = k < ntl;
+      int mi = 0, ni = 0;
+      if (tile_live) tile_coords(bid + k * grid, tm, tn, &mi, &ni);
+      ga = mi * (kBM / 16) + p * 4;
+      gb = ni * (kBN / 16) + p * 4;
+      sa_row = mi * kBM + p * 64 + lane;
+      sb_row = ni * kBN + p * 64 + lane;
+    };
+    int ik = 0, is = 0;                                        // next stage to copy
+    set_tile(0);
+    auto issue = [&](int buf) {
       const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
-      const bool live = s < nslices;
-      int al = a_lane, bl = b_lane, sal = sa_row * 4, sbl = sb_row * 4;
+      int al = ga * nslices * 1024 + lane * 16, bl = gb * nslices * 1024 + lane * 16;
+      int sal = sa_row * 4, sbl = sb_row * 4;
       asm volatile("" : "+v"(al), "+v"(bl), "+v"(sal), "+v"(sbl));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int off = (j * nslices + s) * 1024;
+        const int off = (j * nslices + is) * 1024;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 4 + j) * 1024));
-        dma_load16(rsrc_a, (live && (ga + j) * 16 < mp) ? al + off : a_bytes, dst);
-        dma_load16(rsrc_b, (live && (gb + j) * 16 < np) ? bl + off : b_bytes, dst + kStageA);
+        dma_load16(rsrc_a, (tile_live && (ga + j) * 16 < mp) ? al + off : a_bytes, dst);
+        dma_load16(rsrc_b, (tile_live && (gb + j) * 16 < np) ? bl + off : b_bytes, dst + kStageA);
       }
-      dma_load4(rsrc_sa, (live && sa_row < mp) ? sal + s * mp * 4 : sa_bytes,
+      dma_load4(rsrc_sa, (tile_live && sa_row < mp) ? sal + is * mp * 4 : sa_bytes,
                 __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kStageA + kStageB + p * 256)));
-      dma_load4(rsrc_sb, (live && sb_row < np) ? sbl + s * np * 4 : sb_bytes,
+      dma_load4(rsrc_sb, (tile_live && sb_row < np) ? sbl + is * np * 4 : sb_bytes,
                 __builtin_amdgcn_readfirstlane(
                     stage + (uint32_t)(kStageA + kStageB + kStageSA + p * 256)));
+      if (++is == nslices) {
+        is = 0;
+        set_tile(++ik);
+      }
     };
-    for (int s = 0; s < kAhead; ++s) issue(s, s);
-    for (int s = 0; s < nslices; ++s) {
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // own part of stage s landed
-      __syncthreads();                                     // stage s visible; s - 1 free
-      issue(s + kAhead, (s + kAhead) & 3);
+    for (int G = 0; G < kAhead; ++G) issue(G);
+    for (int G = 0; G < total; ++G) {
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // own part of stage G landed
+      __syncthreads();                                     // stage G visible; G - 1 free
+      issue((G + kAhead) & 3);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // zero-fill loads past the end
-  } else {
-    const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
-    const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
-    const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
-    const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
-    for (int s = 0; s < nslices; ++s) {
-      __syncthreads();                                     // stage s landed
-      const uint8_t *base = smem + (s & 3) * kStageBytes;
-      uint4 bf[4];
-      uint32_t sb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
-        sb[j] = *reinterpret_cast<const uint32_t *>(base + sb_off + j * 64) >> (8 * lg);
-      }
-      uint4 af = *reinterpret_cast<const uint4 *>(base + a_off);
-      uint32_t sa = *reinterpret_cast<const uint32_t *>(base + sa_off) >> (8 * lg);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint4 af_next = af;
-        uint32_t sa_next = sa;
-        if (i + 1 < 8) {
-          af_next = *reinterpret_cast<const uint4 *>(base + a_off + (i + 1) * 1024);
-          sa_next = *reinterpret_cast<const uint32_t *>(base + sa_off + (i + 1) * 64) >> (8 * lg);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af, acc[i][j], sb[j], sa);
-        af = af_next;
-        sa = sa_next;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    return;
   }
 
-  // Epilogue. Fast path (N and ldc multiples of 8, C 16-byte aligned): the tile goes through the now idle LDS
-  // ring in row-major order and leaves as whole 512-byte (bf16) or 1 KB
-  // (fp32) rows, one 16-byte store per lane, so every store instruction
-  // writes complete cache lines.
-  const bool fast_epi = (g.N & 7) == 0 && (g.ldc & 7) == 0 &&
-                        (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
-  if (fast_epi) {
-    constexpr int kEsz = OUT_BF16 ? 2 : 4;
-    constexpr int kRowB = kBN * kEsz;                // bytes of one tile row
-    constexpr int kPitch = kRowB + 16;               // padded LDS row
-    constexpr int kRowsPerPass = OUT_BF16 ? 256 : 128;
-    static_assert(kRowsPerPass * kPitch <= kRing * kStageBytes, "epilogue staging fits the ring");
-    const int64_t rows_left = g.M - m0;
-    const int cols_left = (int)min((int64_t)kBN, g.N - n0);
+  // consumers
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) &&
+                      ((g.ldc & 3) == 0);
+  const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
+  const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
+  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
+  v4f acc[8][4];
 #pragma unroll
-    for (int h = 0; h < 256 / kRowsPerPass; ++h) {
-      __syncthreads();                               // ring (or previous pass) no longer read
-      if (!producer && (OUT_BF16 || wm == h)) {
-        const int rbase = OUT_BF16 ? wm * 128 : 0;
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  int ck = 0, cs = 0;
+  for (int G = 0; G < total; ++G) {
+    __syncthreads();                                       // stage G landed
+    const uint8_t *base = smem + (G & 3) * kStageBytes;
+    uint4 bf[4];
+    uint32_t sb[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint8_t *p = smem + (rbase + i * 16 + lr) * kPitch + (wn * 64 + j * 16 + 4 * lg) * kEsz;
-            if (OUT_BF16) {
-              uint2 v;
-              v.x = (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
-              v.y = (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
-              *reinterpret_cast<uint2 *>(p) = v;
-            } else {
-              *reinterpret_cast<float4 *>(p) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            }
-          }
-      }
-      __syncthreads();
-      // 16 bytes per thread: kRowB / 16 threads per row
-      constexpr int kThrPerRow = kRowB / 16;
-      constexpr int kRowsPerIter = kThreads / kThrPerRow;
-      const int r_in = tid / kThrPerRow, c16 = tid % kThrPerRow;
-#pragma unroll 4
-      for (int r = r_in; r < kRowsPerPass; r += kRowsPerIter) {
-        const int trow = h * kRowsPerPass + r;
-        const int col = c16 * (16 / kEsz);
-        if (trow < rows_left && col < cols_left) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(smem + r * kPitch + c16 * 16);
-          uint8_t *dst = reinterpret_cast<uint8_t *>(g.c) + ((m0 + trow) * g.ldc + n0 + col) * kEsz;
-          *reinterpret_cast<uint4 *>(dst) = v;
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
+      sb[j] = *reinterpret_cast<const uint32_t *>(base + sb_off + j * 64) >> (8 * lg);
     }
-  } else if (!producer) {
+    uint4 af = *reinterpret_cast<const uint4 *>(base + a_off);
+    uint32_t sa = *reinterpret_cast<const uint32_t *>(base + sa_off) >> (8 * lg);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      uint4 af_next = af;
+      uint32_t sa_next = sa;
+      if (i + 1 < 8) {
+        af_next = *reinterpret_cast<const uint4 *>(base + a_off + (i + 1) * 1024);
+        sa_next = *reinterpret_cast<const uint32_t *>(base + sa_off + (i + 1) * 64) >> (8 * lg);
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        store_quad<OUT_BF16>(g, acc[i][j], (int64_t)m0 + wm * 128 + i * 16 + lr,
-                             (int64_t)n0 + wn * 64 + j * 16 + 4 * lg);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af, acc[i][j], sb[j], sa);
+      af = af_next;
+      sa = sa_next;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (++cs == nslices) {
+      cs = 0;
+      int mi, ni;
+      tile_coords(bid + ck * grid, tm, tn, &mi, &ni);
+      ++ck;
+      const int64_t row0 = (int64_t)mi * kBM + wm * 128 + lr;
+      const int64_t col0 = (int64_t)ni * kBN + wn * 64 + 4 * lg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
+          acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   }
 }
 
@@ -321,6 +323,20 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(GemmArgs g) {
 
 }  // namespace
 
+// Compute units of the current device (one persistent workgroup each).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
   if (g.K == 0) {
     const int64_t total = g.M * g.N;
@@ -329,7 +345,7 @@ hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
                       : launch(fill_zero_kernel<0>, grid, dim3(256), 0, stream, g);
   }
   const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-  const dim3 grid((unsigned)tiles);
+  const dim3 grid((unsigned)std::min<int64_t>(tiles, cu_count()));
   return g.out_bf16 ? launch(gemm_tiled_kernel<1>, grid, dim3(kThreads), 0, stream, g)
                     : launch(gemm_tiled_kernel<0>, grid, dim3(kThreads), 0, stream, g);
 }

@@ -240,11 +240,12 @@ def test_gemm_several_tiles(mx):
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("pad", [8, 4, 0])
+@pytest.mark.parametrize("pad", [8, 4, 0, 1])
 def test_gemm_strided_out(mx, out_dtype, pad):
-    """Row-strided output: ldc = N + pad. pad 8 (and 0) takes the row-staged
-    epilogue, pad 4 the element-wise one; both must give the contiguous
-    result bit for bit and leave the pad columns untouched."""
+    """Row-strided output: ldc = N + pad (the vector quad stores need ldc a
+    multiple of 4; odd N and ldc take the element-wise stores in
+    test_gemm_lds_path_tails). The result must equal the contiguous one bit
+    for bit and the pad columns stay untouched."""
     import torch
     rng = np.random.default_rng(31 + pad)
     M, N, K = 300, 264, 384
