@@ -78,19 +78,26 @@ typedef enum mx_out_dtype { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out_dtype;
  *   MN = rows, K = cols   when axis == 1 (blocks run along a row);
  *   MN = cols, K = rows   when axis == 0 (blocks run down a column; the
  *                         source is written out transposed).
- * It is zero-padded to MNp = MN rounded up to 16 and Kp = K rounded up to
- * 128, and stored in 16 x 128 tiles, the fragment shape of the gfx950 FP4
- * matrix instruction, so the GEMM streams every tile as one contiguous 1 KB:
+ * It is zero-padded to MNp = MN rounded up to 256 (whole 256-row panels, the
+ * GEMM's block height) and Kp = K rounded up to 128, and stored in 16 x 128
+ * tiles, the fragment shape of the gfx950 FP4 matrix instruction, so the GEMM
+ * streams every tile as one contiguous 1 KB:
  *   codes : MNp * Kp / 2 bytes. Tile (g, q) -- rows 16g..16g+15, K elements
  *           128q..128q+127 -- is the 1 KB at byte (g * Kp/128 + q) * 1024;
  *           inside it, 32-element block c (0..3) of row r (0..15) is the 16
  *           bytes at c * 256 + r * 16, two codes per byte, the even K index in
  *           the low nibble. Code = sign << 3 | E2M1 magnitude code (0..7 for
  *           0, 0.5, 1, 1.5, 2, 3, 4, 6).
- *   scales: MNp * Kp / 32 bytes, [Kp/128][MNp][4]: the E8M0 code s (value
- *           2^(s-127)) of block kb of row mn is at byte
- *           ((kb / 4) * MNp + mn) * 4 + kb % 4. 0xFF marks a block that held a
- *           NaN or Inf (its codes are 0).
+ *   scales: MNp * Kp / 32 bytes, [Kp/128][MNp/256][16][4][16]: the E8M0
+ *           code s (value 2^(s-127)) of block kb = 4q + c of row
+ *           mn = 256T + 16h + r is at byte
+ *           ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h. One 1 KB block per
+ *           K slice and 256-row panel; inside it, for a fixed (r, c), the
+ *           scales of the panel's 16 row groups are 16 consecutive bytes, so
+ *           the scales a matrix-instruction lane needs for consecutive row
+ *           groups are consecutive bytes of one register (picked by the
+ *           instruction's byte select). 0xFF marks a block that held a NaN or
+ *           Inf (its codes are 0).
  * Padding rows and blocks hold the encoding of zeros (codes 0, scale code 0).
  * Element value = (-1)^sign * E2M1(mag) * 2^(s - 127).
  */

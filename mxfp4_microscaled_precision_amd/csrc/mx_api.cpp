@@ -43,7 +43,7 @@ void padded_extents(int64_t rows, int64_t cols, int32_t axis, int64_t *mnp, int6
   const int64_t mn = axis == 1 ? rows : cols;
   const int64_t k = axis == 1 ? cols : rows;
   const bool empty = rows == 0 || cols == 0;
-  *mnp = empty ? 0 : (mn + 15) / 16 * 16;
+  *mnp = empty ? 0 : (mn + 255) / 256 * 256;
   *kp = empty ? 0 : (k + 127) / 128 * 128;
 }
 

@@ -12,7 +12,8 @@
 // supplies row (l % 16) of A and row (l % 16) of B, K elements
 // [32 * (l / 16), 32 * (l / 16) + 32) as 16 packed bytes (element 2j in the
 // low nibble of byte j), and the E8M0 scale of exactly that 32-element block
-// in byte 0 of its scale operand; lane l receives rows 4 * (l / 16) + r,
+// in a byte of its scale operand chosen by the instruction's byte select;
+// lane l receives rows 4 * (l / 16) + r,
 // r = 0..3, of output column l % 16. The kernel passes B as the first
 // operand, so lane l holds C[l % 16][4 * (l / 16) + r]: four consecutive
 // columns of one row.
@@ -21,6 +22,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <utility>
 
 #include "mx_kernels.h"
 
@@ -34,12 +36,15 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp4 = 4;
 
+// One 16x16x128 FP4 MFMA. The E8M0 scale of each operand is byte SELA / SELB
+// of the given register (the instruction's byte select).
+template <int SELA, int SELB>
 __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, v4f c, uint32_t sa,
                                         uint32_t sb) {
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, kFmtFp4, kFmtFp4, 0,
-                                                          (int)sa, 0, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, kFmtFp4, kFmtFp4, SELA,
+                                                          (int)sa, SELB, (int)sb);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -171,6 +176,28 @@ __device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc
   }
 }
 
+// Row I of a consumer's stage: read A fragment I + 1, then the 4 MFMAs of
+// row I (reading two rows ahead was measured slower on Wgrad and Dgrad). B is the first MFMA operand (its scale byte j of sb), A the second
+// (scale byte I % 4 of sa.x for rows 0..3, of sa.y for rows 4..7).
+template <int I>
+__device__ __forceinline__ void consume_row(v4f (&acc)[8][4], const uint4 (&bf)[4], uint4 (&af)[8],
+                                            const uint8_t *a_base, uint32_t sb, uint2 sa) {
+  if (I + 1 < 8) af[I + 1 < 8 ? I + 1 : 0] = *reinterpret_cast<const uint4 *>(a_base + (I + 1) * 1024);
+  const uint32_t sai = I < 4 ? sa.x : sa.y;
+  acc[I][0] = mfma_fp4<0, I & 3>(bf[0], af[I], acc[I][0], sb, sai);
+  acc[I][1] = mfma_fp4<1, I & 3>(bf[1], af[I], acc[I][1], sb, sai);
+  acc[I][2] = mfma_fp4<2, I & 3>(bf[2], af[I], acc[I][2], sb, sai);
+  acc[I][3] = mfma_fp4<3, I & 3>(bf[3], af[I], acc[I][3], sb, sai);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int... I>
+__device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v4f (&acc)[8][4],
+                                             const uint4 (&bf)[4], uint4 (&af)[8],
+                                             const uint8_t *a_base, uint32_t sb, uint2 sa) {
+  (consume_row<I>(acc, bf, af, a_base, sb, sa), ...);
+}
+
 // Persistent: one workgroup per compute unit walks the tiles bid, bid + grid,
 // ... as one continuous sequence of stages; producers run three stages ahead
 // across tile boundaries, and consumers store a finished tile while the next
@@ -188,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int tiles = tm * tn;
   const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
   const int ntl = (tiles - bid + grid - 1) / grid;             // tiles of this workgroup
-  const int mp = (int)((g.M + 15) & ~15LL), np = (int)((g.N + 15) & ~15LL);   // padded rows
+  const int mp = (int)((g.M + 255) & ~255LL), np = (int)((g.N + 255) & ~255LL);   // padded rows
   const int nslices = (int)((g.K + 127) >> 7);
   const int total = ntl * nslices;                             // stages of this workgroup
   const uint32_t smem_base = (uint32_t)reinterpret_cast<uintptr_t>(smem);
@@ -196,17 +223,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int lg = lane >> 4;      // 32-element K block within the slice
 
   if (producer) {
-    // Producer p copies row groups 4p .. 4p + 3 of A and of B and scale rows
-    // 64p .. 64p + 63 of A and of B: ten DMA instructions per stage. Stages
-    // past the last one read zeros so the counts stay uniform.
+    // Producer p copies row groups 4p .. 4p + 3 of A and of B (eight 1 KB
+    // tiles); producer 0 also copies the stage's A scales and producer 1 its
+    // B scales: the 1 KB block of (K slice, 256-row panel), in which lane
+    // l = 4 r + c takes the 16 bytes of row-in-group r, block c for the
+    // panel's 16 row groups. Stages past the last one read zeros so the
+    // counts stay uniform.
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
     const v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
     const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
-    const v4i rsrc_sa = make_rsrc(g.a_scales, (uint32_t)sa_bytes);
-    const v4i rsrc_sb = make_rsrc(g.b_scales, (uint32_t)sb_bytes);
-    int ga = 0, gb = 0, sa_row = 0, sb_row = 0;
+    const v4i rsrc_s = p == 0 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
+                              : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+    const int s_panels = (p == 0 ? mp : np) >> 8;              // 256-row panels
+    const int s_bytes = p == 0 ? sa_bytes : sb_bytes;
+    const int s_lane = lane * 16;
+    int ga = 0, gb = 0, gs = 0;
     bool tile_live = false;
     auto set_tile = [&](int k) {
       tile_live = k < ntl;
@@ -214,28 +247,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
       if (tile_live) tile_coords(bid + k * grid, tm, tn, &mi, &ni);
       ga = mi * (kBM / 16) + p * 4;
       gb = ni * (kBN / 16) + p * 4;
-      sa_row = mi * kBM + p * 64 + lane;
-      sb_row = ni * kBN + p * 64 + lane;
+      gs = p == 0 ? mi : ni;                                   // the tile's panel
     };
     int ik = 0, is = 0;                                        // next stage to copy
     set_tile(0);
     auto issue = [&](int buf) {
       const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
       int al = ga * nslices * 1024 + lane * 16, bl = gb * nslices * 1024 + lane * 16;
-      int sal = sa_row * 4, sbl = sb_row * 4;
-      asm volatile("" : "+v"(al), "+v"(bl), "+v"(sal), "+v"(sbl));
+      int sl = s_lane + gs * 1024;
+      asm volatile("" : "+v"(al), "+v"(bl), "+v"(sl));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int off = (j * nslices + is) * 1024;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 4 + j) * 1024));
-        dma_load16(rsrc_a, (tile_live && (ga + j) * 16 < mp) ? al + off : a_bytes, dst);
-        dma_load16(rsrc_b, (tile_live && (gb + j) * 16 < np) ? bl + off : b_bytes, dst + kStageA);
+        dma_load16(rsrc_a, tile_live ? al + off : a_bytes, dst);
+        dma_load16(rsrc_b, tile_live ? bl + off : b_bytes, dst + kStageA);
       }
-      dma_load4(rsrc_sa, (tile_live && sa_row < mp) ? sal + is * mp * 4 : sa_bytes,
-                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kStageA + kStageB + p * 256)));
-      dma_load4(rsrc_sb, (tile_live && sb_row < np) ? sbl + is * np * 4 : sb_bytes,
-                __builtin_amdgcn_readfirstlane(
-                    stage + (uint32_t)(kStageA + kStageB + kStageSA + p * 256)));
+      if (p < 2)
+        dma_load16(rsrc_s, tile_live ? sl + is * s_panels * 1024 : s_bytes,
+                   __builtin_amdgcn_readfirstlane(
+                       stage + (uint32_t)(kStageA + kStageB + (p == 0 ? 0 : kStageSA))));
       if (++is == nslices) {
         is = 0;
         set_tile(++ik);
@@ -243,7 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     };
     for (int G = 0; G < kAhead; ++G) issue(G);
     for (int G = 0; G < total; ++G) {
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // own part of stage G landed
+      // own part of stage G landed: nine copies per stage on producers 0
+      // and 1, eight on 2 and 3, two later stages outstanding
+      if (p < 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
       __syncthreads();                                     // stage G visible; G - 1 free
       issue((G + kAhead) & 3);
     }
@@ -256,8 +292,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
                       ((g.ldc & 3) == 0);
   const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
-  const uint32_t sa_off = (uint32_t)(kStageA + kStageB + (wm * 128 + lr) * 4);
-  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA + (wn * 64 + lr) * 4);
+  // scales: slot 4 lr + lg holds the 16 row groups' bytes of row-in-group lr,
+  // block lg; this wave's A rows are groups 8 wm .. 8 wm + 7, its B rows
+  // groups 4 wn .. 4 wn + 3
+  const uint32_t s_slot = (uint32_t)((lr * 4 + lg) * 16);
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + s_slot + wm * 8;
+  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + s_slot + wn * 4;
   v4f acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -267,29 +307,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   for (int G = 0; G < total; ++G) {
     __syncthreads();                                       // stage G landed
     const uint8_t *base = smem + (G & 3) * kStageBytes;
-    uint4 bf[4];
-    uint32_t sb[4];
+    uint4 bf[4], af[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
-      sb[j] = *reinterpret_cast<const uint32_t *>(base + sb_off + j * 64) >> (8 * lg);
-    }
-    uint4 af = *reinterpret_cast<const uint4 *>(base + a_off);
-    uint32_t sa = *reinterpret_cast<const uint32_t *>(base + sa_off) >> (8 * lg);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 af_next = af;
-      uint32_t sa_next = sa;
-      if (i + 1 < 8) {
-        af_next = *reinterpret_cast<const uint4 *>(base + a_off + (i + 1) * 1024);
-        sa_next = *reinterpret_cast<const uint32_t *>(base + sa_off + (i + 1) * 64) >> (8 * lg);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(bf[j], af, acc[i][j], sb[j], sa);
-      af = af_next;
-      sa = sa_next;
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
+    const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + sb_off);
+    const uint2 sa = *reinterpret_cast<const uint2 *>(base + sa_off);
+    af[0] = *reinterpret_cast<const uint4 *>(base + a_off);
+    // rows of 4 MFMAs, A fragments one row ahead
+    consume_rows(std::make_integer_sequence<int, 8>{}, acc, bf, af, base + a_off, sb, sa);
     if (++cs == nslices) {
       cs = 0;
       int mi, ni;

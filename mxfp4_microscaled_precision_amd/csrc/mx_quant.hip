@@ -260,17 +260,19 @@ __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_
 
 // ---------------------------------------------------------------------------
 // Output layout (tiled, see mx_qtensor in mxfp4.h): the operand is viewed
-// reduction-major, [MN, K], zero-padded to [MNp, Kp] (MNp multiple of 16, Kp
+// reduction-major, [MN, K], zero-padded to [MNp, Kp] (MNp multiple of 256, Kp
 // of 128). Codes: tile (g, q) = rows 16g.., K elements 128q.. is 1 KB at
 // (g * Kp/128 + q) * 1024, block c of row r at c * 256 + r * 16 inside it.
-// Scales: [Kp/128][MNp][4]. Padding positions hold the encoding of zeros
-// (codes 0, scale code 0).
+// Scales: [Kp/128][MNp/256][16][4][16], the scale of row 256T + 16h + r,
+// block 4q + c at ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h. Padding
+// positions hold the encoding of zeros (codes 0, scale code 0).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t code_offset(int64_t mn, int64_t kb, int64_t nslices) {
   return ((mn >> 4) * nslices + (kb >> 2)) * 1024 + (kb & 3) * 256 + (mn & 15) * 16;
 }
 __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t mnp) {
-  return ((kb >> 2) * mnp + mn) * 4 + (kb & 3);
+  return (((kb >> 2) * (mnp >> 8) + (mn >> 8)) * 16 + (mn & 15)) * 64 + (kb & 3) * 16 +
+         ((mn >> 4) & 15);
 }
 
 // ---------------------------------------------------------------------------
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     uint32_t seed_hi) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][4096];
   __shared__ __attribute__((aligned(16))) uint8_t signs_lds[ROT == MX_K_ROT_RAND_SIGN ? 4 : 1][128];
-  const int64_t mnp = (rows + 15) & ~(int64_t)15;
+  const int64_t mnp = (rows + 255) & ~(int64_t)255;
   const int64_t nslices = (cols + 127) >> 7;
   const int64_t ntiles = (mnp >> 4) * nslices;
   const int wv = threadIdx.x >> 6;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
     uint32_t seed_hi, int rb, int pair_loads) {
-  const int64_t mnp = (cols + 15) & ~(int64_t)15;
+  const int64_t mnp = (cols + 255) & ~(int64_t)255;
   const int64_t nslices = (rows + 127) >> 7;
   const int64_t nkb_pad = nslices * 4;
   const int64_t nkb = rows >> 5;
@@ -489,6 +491,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   const int64_t C0 = bx * 128, R0 = by * 32;
   const int64_t nsl1 = (cols + 127) >> 7;   // axis-1 operand: MN = rows, K = cols
   const int64_t nsl0 = (rows + 127) >> 7;   // axis-0 operand: MN = cols, K = rows
+  const int64_t mnp1 = (rows + 255) & ~(int64_t)255, mnp0 = (cols + 255) & ~(int64_t)255;
   const bool rows_live = R0 < rows;
 
   if (rows_live) {
@@ -509,11 +512,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   uint32_t out[4];
   uint32_t s;
   if (tid < 128) {
-    if (!rows_live) return;
-    // axis 1: row R0 + rr, 32-block kb along the columns
+    // axis 1: row R0 + rr (< mnp1), 32-block kb along the columns
     const int rr = tid & 31, b = tid >> 5;
     const int64_t r = R0 + rr;
     const int64_t kb = (C0 >> 5) + b;
+    if (kb >= nsl1 * 4) return;                           // past the operand's K extent
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((b * 4 + j) ^ (rr & 15)) << 4));
@@ -532,21 +535,21 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       return pick_word(w, (uint32_t)(i & 3)) >> 8;
     };
     s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
-    if ((kb << 5) >= cols) {                              // K padding of the operand
+    if ((kb << 5) >= cols || !rows_live) {                // padding of the operand
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = 0u;
       s = 0u;
     }
     *reinterpret_cast<uint4 *>(codes1 + code_offset(r, kb, nsl1)) =
         make_uint4(out[0], out[1], out[2], out[3]);
-    scales1[scale_offset(r, kb, rows)] = (uint8_t)s;
+    scales1[scale_offset(r, kb, mnp1)] = (uint8_t)s;
   } else {
     // axis 0: column C0 + cc, 32-block R0 / 32 along the rows
     const int cc = tid - 128;
-    const int64_t c = C0 + cc;
-    if (c >= cols) return;
+    const int64_t c = C0 + cc;                            // < mnp0
     const int64_t kb = R0 >> 5;
-    if (rows_live) {
+    if (kb >= nsl0 * 4) return;                           // past the operand's K extent
+    if (rows_live && c < cols) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const uint16_t bits =
@@ -567,14 +570,17 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     }
     *reinterpret_cast<uint4 *>(codes0 + code_offset(c, kb, nsl0)) =
         make_uint4(out[0], out[1], out[2], out[3]);
-    scales0[scale_offset(c, kb, cols)] = (uint8_t)s;
+    scales0[scale_offset(c, kb, mnp0)] = (uint8_t)s;
   }
 }
 
 template <int ROT, int RND>
 hipError_t launch_dual(const DualArgs &a, hipStream_t stream) {
-  const int64_t gx = (a.cols + 127) / 128;
-  const int64_t gy = ((a.rows + 127) >> 7) * 4;          // K blocks of the axis-0 operand
+  // columns up to the axis-0 operand's padded MN extent (which covers the
+  // axis-1 operand's K extent), rows up to the axis-1 operand's padded MN
+  // extent (which covers the axis-0 operand's K extent)
+  const int64_t gx = ((a.cols + 255) & ~(int64_t)255) / 128;
+  const int64_t gy = ((a.rows + 255) & ~(int64_t)255) / 32;
   return launch(quant_dual_kernel<ROT, RND>, dim3((unsigned)(gx * gy)), dim3(256), 0, stream,
                 a.x, a.rows, a.cols, a.ld, a.codes1, a.scales1, a.seed1_lo, a.seed1_hi,
                 a.codes0, a.scales0, a.seed0_lo, a.seed0_hi, gx);
@@ -583,14 +589,14 @@ hipError_t launch_dual(const DualArgs &a, hipStream_t stream) {
 template <int ROT, int RND>
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
-    const int64_t mnp = (a.rows + 15) & ~(int64_t)15;
+    const int64_t mnp = (a.rows + 255) & ~(int64_t)255;
     const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
     const int64_t blocks = (ntiles + 3) / 4;
     return launch(quant_axis1_kernel<ROT, RND>, dim3((unsigned)blocks), dim3(256), 0, stream,
                   a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi);
   }
   const int threads = 256;
-  const int64_t mnp = (a.cols + 15) & ~(int64_t)15;
+  const int64_t mnp = (a.cols + 255) & ~(int64_t)255;
   const int64_t gx = (mnp / 2 + threads - 1) / threads;
   const int64_t nkb_pad = ((a.rows + 127) >> 7) * 4;
   const int rb = a.rb > 0 ? a.rb : 4;

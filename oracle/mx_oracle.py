@@ -96,6 +96,7 @@ __all__ = [
     "unpack_codes",
     "TILE_ROWS",
     "TILE_K",
+    "PANEL_ROWS",
     "padded_extents",
     "tile_codes",
     "tile_scales",
@@ -435,11 +436,12 @@ def pack_codes(codes: np.ndarray) -> np.ndarray:
 
 TILE_ROWS = 16      # reduction-major rows per tile
 TILE_K = 128        # reduction elements per tile (four 32-element blocks)
+PANEL_ROWS = 256    # MN is padded to whole panels of 256 rows
 
 
 def padded_extents(mn: int, k: int) -> Tuple[int, int]:
-    """Extents of the tiled layout: MN up to a multiple of 16, K of 128."""
-    return -(-mn // TILE_ROWS) * TILE_ROWS, -(-k // TILE_K) * TILE_K
+    """Extents of the tiled layout: MN up to a multiple of 256, K of 128."""
+    return -(-mn // PANEL_ROWS) * PANEL_ROWS, -(-k // TILE_K) * TILE_K
 
 
 def tile_codes(codes: np.ndarray) -> np.ndarray:
@@ -462,14 +464,22 @@ def tile_codes(codes: np.ndarray) -> np.ndarray:
 
 
 def tile_scales(scales: np.ndarray, k: int) -> np.ndarray:
-    """Scales [MN, K/32] -> tiled buffer [Kp/128][MNp][4] (padding scale code 0,
-    the code of an all-zero block)."""
+    """Scales [MN, K/32] -> tiled buffer [Kp/128][MNp/256][16][4][16] (padding
+    scale code 0, the code of an all-zero block).
+
+    The scale of row m = 256 T + 16 h + r (panel T, row group h inside it, row
+    r) and block kb = 4 q + c is the byte at
+    ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h: one 1 KB block per K slice
+    and 256-row panel, in which the scales of the panel's 16 row groups for a
+    fixed (r, c) are 16 consecutive bytes.
+    """
     scales = np.asarray(scales, dtype=np.uint8)
     mn = scales.shape[0]
     mnp, kp = padded_extents(mn, k)
     full = np.zeros((mnp, kp // 32), np.uint8)
     full[:mn, :scales.shape[1]] = scales
-    return np.ascontiguousarray(full.reshape(mnp, kp // TILE_K, 4).transpose(1, 0, 2)).reshape(-1)
+    t = full.reshape(mnp // PANEL_ROWS, PANEL_ROWS // TILE_ROWS, TILE_ROWS, kp // TILE_K, 4)  # T h r q c
+    return np.ascontiguousarray(t.transpose(3, 0, 2, 4, 1)).reshape(-1)                     # q T r c h
 
 
 def untile_codes(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
@@ -484,8 +494,9 @@ def untile_codes(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
 def untile_scales(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
     """Inverse of tile_scales: tiled bytes -> scales [MN, K/32]."""
     mnp, kp = padded_extents(mn, k)
-    t = np.asarray(buf, np.uint8)[: mnp * kp // 32].reshape(kp // TILE_K, mnp, 4)
-    return t.transpose(1, 0, 2).reshape(mnp, kp // 32)[:mn, : k // 32]
+    t = np.asarray(buf, np.uint8)[: mnp * kp // 32].reshape(
+        kp // TILE_K, mnp // PANEL_ROWS, TILE_ROWS, 4, PANEL_ROWS // TILE_ROWS)      # q T r c h
+    return t.transpose(1, 4, 2, 0, 3).reshape(mnp, kp // 32)[:mn, : k // 32]
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:

@@ -39,10 +39,11 @@ def test_version_and_status_strings():
 
 def test_quantize_sizes():
     assert mx.quantize_sizes(8192, 4096, 1) == (8192 * 4096 // 2, 8192 * 4096 // 32)
-    # tiled layout: MN padded to 16, K to 128
-    assert mx.quantize_sizes(256, 96, 0) == (96 * 256 // 2, 96 * 256 // 32)
-    assert mx.quantize_sizes(37, 160, 1) == (48 * 256 // 2, 48 * 256 // 32)
-    assert mx.quantize_sizes(160, 37, 0) == (48 * 256 // 2, 48 * 256 // 32)
+    # tiled layout: MN padded to 256, K to 128
+    assert mx.quantize_sizes(256, 96, 0) == (256 * 256 // 2, 256 * 256 // 32)
+    assert mx.quantize_sizes(37, 160, 1) == (256 * 256 // 2, 256 * 256 // 32)
+    assert mx.quantize_sizes(160, 37, 0) == (256 * 256 // 2, 256 * 256 // 32)
+    assert mx.quantize_sizes(300, 128, 1) == (512 * 128 // 2, 512 * 128 // 32)
     assert mx.quantize_sizes(0, 0, 1) == (0, 0)
     assert mx.quantize_sizes(0, 64, 1) == (0, 0)
     for args, code in [((64, 48, 1), -2), ((48, 64, 0), -2), ((64, 64, 2), -4),

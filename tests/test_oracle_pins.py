@@ -491,13 +491,15 @@ def test_tiled_layout_addresses_and_roundtrip():
     """Every element's byte address in the tiled buffer follows the layout
     formula (written here as an explicit loop), and untile inverts tile."""
     rng = np.random.default_rng(13)
-    for mn, k in ((37, 160), (16, 128), (5, 32), (33, 256)):
+    for mn, k in ((37, 160), (16, 128), (5, 32), (33, 256), (300, 128)):
         codes = rng.integers(0, 16, (mn, k)).astype(np.uint8)
         scales = rng.integers(0, 255, (mn, k // 32)).astype(np.uint8)
         tb = oracle.tile_codes(codes)
         sb = oracle.tile_scales(scales, k)
         mnp, kp = oracle.padded_extents(mn, k)
         assert tb.size == mnp * kp // 2 and sb.size == mnp * kp // 32
+        assert mnp % 256 == 0 and mnp >= mn and mnp - mn < 256
+        NT = mnp // 256
         for m in range(mn):
             for kk in range(0, k, 7):
                 g, r, q, c = m // 16, m % 16, kk // 128, (kk % 128) // 32
@@ -505,7 +507,8 @@ def test_tiled_layout_addresses_and_roundtrip():
                 nib = (tb[byte] >> 4) if kk % 2 else (tb[byte] & 15)
                 assert nib == codes[m, kk]
             for kb in range(k // 32):
-                assert sb[((kb // 4) * mnp + m) * 4 + kb % 4] == scales[m, kb]
+                T, h, r, q, c = m // 256, (m // 16) % 16, m % 16, kb // 4, kb % 4
+                assert sb[((q * NT + T) * 16 + r) * 64 + c * 16 + h] == scales[m, kb]
         # padding: zero codes, scale code 0
         full = oracle.untile_codes(tb, mnp, kp)
         assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
