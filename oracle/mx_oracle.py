@@ -43,6 +43,13 @@ What the pages fix, and the readings taken where they are silent:
   * [36Kr] "Fehlerdiagnoseexperiment": Fprop Y = X W^T, Dgrad dX = dY W,
     Wgrad dW = dY^T X. The GEMM is the exact sum over dequantized values,
     evaluated here in fp64.
+  * Comparator: [36Kr] intro and "Ende-zu-Ende-Effizienz" measure MXFP4
+    against FP8; [ShowAPI] section 2.2 names E4M3 and E5M2 as the FP8
+    formats. Reading: the FP8 comparator is MXFP8 with E4M3 elements (OCP:
+    bias 7, subnormals, 448 largest, NaN at S.1111.111, no Inf), the same
+    32-element blocks and E8M0 scale, block exponent floor(log2 amax) - 8,
+    elements rounded to nearest even and saturated at 448. Only RNE: the
+    pages compare stochastic rounding within MXFP4, not within FP8.
 
 What pins each function (tests/test_oracle_*.py, all "not gpu"):
   e2m1_value            OCP E2M1 table (tests/golden/e2m1_table.txt) and the
@@ -67,6 +74,13 @@ What pins each function (tests/test_oracle_*.py, all "not gpu"):
   dequantize_ref,
   mx_gemm_ref           explicit triple loop and exact fractions.Fraction sums;
                         the rotation cancels in the product.
+  e4m3_value            torch.float8_e4m3fn decode of all 256 codes.
+  round_e4m3_rne        torch's fp32 -> float8_e4m3fn conversion on every
+                        midpoint and its neighbours; brute-force nearest
+                        search; saturation at 448.
+  quantize_ref (fp8)    worked one-hot (H32) / constant / zero / NaN blocks;
+                        fixed-point re-quantization; exact-fraction GEMM;
+                        tile_codes_fp8 address loop and round trip.
 """
 from __future__ import annotations
 
@@ -108,6 +122,13 @@ __all__ = [
     "operand_mse",
     "fwht16x2_f32",
     "ROT_HADAMARD16",
+    "FMT_FP4",
+    "FMT_FP8",
+    "e4m3_value",
+    "e4m3_magnitudes",
+    "round_e4m3_rne",
+    "tile_codes_fp8",
+    "untile_codes_fp8",
 ]
 
 MX_BLOCK = 32          # elements per shared exponent ([36Kr] "Was ist MXFP4?")
@@ -119,6 +140,9 @@ ROT_HADAMARD16 = "hadamard16"
 H16_HALF = 16                 # points per transform of the 16-point variant
 H16_C_F32 = np.float32(0.25)  # 1/sqrt(16), exact in fp32
 ROUND_RNE, ROUND_SR = "rne", "sr"
+FMT_FP4, FMT_FP8 = "fp4_e2m1", "fp8_e4m3"   # element formats (MXFP4; MXFP8 comparator)
+E4M3_EMAX = 8          # largest unbiased exponent of E4M3 (OCP reading)
+E4M3_MAX_CODE = 0x7E   # 448 = 1.75 * 2^8; 0x7F is NaN
 
 _M32 = np.uint64(0xFFFFFFFF)
 
@@ -141,6 +165,48 @@ def e2m1_value(code: int) -> float:
 def e2m1_magnitudes() -> np.ndarray:
     """The 8 non-negative E2M1 values, indexed by the 3-bit magnitude code."""
     return np.array([e2m1_value(c) for c in range(8)], dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Comparator element format: E4M3 (OCP MXFP8). The pages compare FP4 with
+# FP8 training ([36Kr] intro: FP4 theoretically twice the compute of FP8;
+# "Ende-zu-Ende-Effizienz": the step-throughput gain over FP8).
+# ---------------------------------------------------------------------------
+def e4m3_value(code: int) -> float:
+    """Value of an 8-bit E4M3 code: sign | 4-bit exponent (bias 7) | 3-bit
+    mantissa; exponent 0 is subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN."""
+    if (code & 0x7F) == 0x7F:
+        return float("nan")
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 3) & 15
+    man = code & 7
+    if exp == 0:
+        mag = man / 8.0 * 2.0 ** -6
+    else:
+        mag = (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return sign * mag
+
+
+def e4m3_magnitudes() -> np.ndarray:
+    """The 127 finite non-negative E4M3 values, indexed by the 7-bit code."""
+    return np.array([e4m3_value(c) for c in range(E4M3_MAX_CODE + 1)], dtype=np.float64)
+
+
+def round_e4m3_rne(a: np.ndarray) -> np.ndarray:
+    """Magnitude code (0..126) of the E4M3 value nearest to a >= 0, ties to
+    the even code (even mantissa bit). Values above 448 go to 448 (the
+    saturating conversion of OCP MX)."""
+    g = e4m3_magnitudes()
+    a64 = np.minimum(np.asarray(a, dtype=np.float32).astype(np.float64), 512.0)
+    flat = a64.reshape(-1)
+    idx = np.clip(np.searchsorted(g, flat, side="right") - 1, 0, E4M3_MAX_CODE)
+    hi = np.minimum(idx + 1, E4M3_MAX_CODE)
+    d_lo = np.abs(flat - g[idx])
+    d_hi = np.abs(g[hi] - flat)
+    code = np.where(d_hi < d_lo, hi, idx)
+    tie = (d_hi == d_lo) & (hi != idx)
+    code = np.where(tie, np.where(idx % 2 == 0, idx, hi), code)
+    return code.reshape(a64.shape).astype(np.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -338,6 +404,7 @@ class QuantRef:
     scales: np.ndarray
     rotated: np.ndarray
     axis: int
+    fmt: str = FMT_FP4
 
 
 def _bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -348,7 +415,7 @@ def quantize_ref(x_bits: np.ndarray, axis: int, block: int = MX_BLOCK,
                  rotate: str = ROT_HADAMARD, rounding: str = ROUND_RNE,
                  seed: int = 0, *, row_index: Optional[np.ndarray] = None,
                  col_index: Optional[np.ndarray] = None,
-                 total_cols: Optional[int] = None) -> QuantRef:
+                 total_cols: Optional[int] = None, fmt: str = FMT_FP4) -> QuantRef:
     """Rotate, scale and round a bfloat16 tensor [R, C] in blocks along `axis`.
 
     row_index / col_index give the global row / column of each supplied row /
@@ -397,11 +464,17 @@ def quantize_ref(x_bits: np.ndarray, axis: int, block: int = MX_BLOCK,
         blocks = fwht32_f32(blocks)
     y = blocks
 
-    # 4. block amax -> 5. E8M0 scale
+    # 4. block amax -> 5. E8M0 scale (the element format's largest exponent
+    #    is taken off: 2 for E2M1, 8 for the E4M3 comparator)
     absy = np.abs(y.astype(np.float64))
     bad = ~np.isfinite(absy).all(axis=-1)
     amax = np.where(bad, 0.0, np.max(np.where(np.isfinite(absy), absy, 0.0), axis=-1))
     e = e8m0_exponent(amax)
+    if fmt == FMT_FP8:
+        e = np.clip(e + E2M1_EMAX - E4M3_EMAX, -127, 127)
+        e = np.where(amax == 0.0, -127, e)
+    elif fmt != FMT_FP4:
+        raise ValueError(fmt)
     scales = (e + 127).astype(np.uint8)
     scales = np.where(bad, np.uint8(0xFF), scales)
 
@@ -412,6 +485,15 @@ def quantize_ref(x_bits: np.ndarray, axis: int, block: int = MX_BLOCK,
     a = np.abs(t)
 
     # 7./8. magnitude code
+    if fmt == FMT_FP8:
+        if rounding != ROUND_RNE:
+            raise ValueError("the E4M3 comparator rounds to nearest even only")
+        mag = round_e4m3_rne(np.where(np.isfinite(a), a, 0.0))
+        sign = np.signbit(y).astype(np.uint8)
+        codes = (sign << 7) | mag
+        codes = np.where(bad[..., None], np.uint8(0), codes).astype(np.uint8)
+        return QuantRef(codes.reshape(MN, K), scales.astype(np.uint8),
+                        y.reshape(MN, K).astype(np.float32), axis, FMT_FP8)
     if rounding == ROUND_RNE:
         mag = round_e2m1_rne(np.where(np.isfinite(a), a, 0.0))
     elif rounding == ROUND_SR:
@@ -482,6 +564,31 @@ def tile_scales(scales: np.ndarray, k: int) -> np.ndarray:
     return np.ascontiguousarray(t.transpose(3, 0, 2, 4, 1)).reshape(-1)                     # q T r c h
 
 
+def tile_codes_fp8(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes [MN, K] (one byte per element) -> tiled byte buffer.
+
+    Zero-padded to [MNp, Kp] like the FP4 layout; tile (g, q) -- rows
+    16g..16g+15, K elements 128q..128q+127 -- is the 2 KB at byte
+    (g * Kp/128 + q) * 2048, and inside it 32-element block c of row r is the
+    32 bytes at c * 512 + r * 32, element i of the block at byte i.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    mn, k = codes.shape
+    mnp, kp = padded_extents(mn, k)
+    full = np.zeros((mnp, kp), np.uint8)
+    full[:mn, :k] = codes
+    t = full.reshape(mnp // TILE_ROWS, TILE_ROWS, kp // TILE_K, 4, 32)     # g r q c byte
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)   # g q c r byte
+
+
+def untile_codes_fp8(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
+    """Inverse of tile_codes_fp8."""
+    mnp, kp = padded_extents(mn, k)
+    t = np.asarray(buf, np.uint8)[: mnp * kp].reshape(mnp // TILE_ROWS, kp // TILE_K, 4,
+                                                      TILE_ROWS, 32)
+    return t.transpose(0, 3, 1, 2, 4).reshape(mnp, kp)[:mn, :k]
+
+
 def untile_codes(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
     """Inverse of tile_codes: tiled bytes -> codes [MN, K]."""
     mnp, kp = padded_extents(mn, k)
@@ -507,11 +614,15 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequantize_ref(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """fp64 values (-1)^s * E2M1(mag) * 2^(scale - 127); scale 0xFF is NaN."""
+def dequantize_ref(codes: np.ndarray, scales: np.ndarray, fmt: str = FMT_FP4) -> np.ndarray:
+    """fp64 values (-1)^s * E2M1(mag) * 2^(scale - 127) (E4M3 for fmt =
+    fp8_e4m3); scale 0xFF is NaN."""
     codes = np.asarray(codes, dtype=np.uint8)
     MN, K = codes.shape
-    table = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    if fmt == FMT_FP8:
+        table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    else:
+        table = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
     vals = table[codes].reshape(MN, K // MX_BLOCK, MX_BLOCK)
     s = np.asarray(scales, dtype=np.int64)
     factor = np.where(s == 0xFF, np.nan, np.ldexp(1.0, s - 127))
@@ -520,13 +631,13 @@ def dequantize_ref(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def mx_gemm_ref(qa: QuantRef, qb: QuantRef) -> np.ndarray:
     """C[m, n] = sum_k deqA[m, k] * deqB[n, k], fp64."""
-    da = dequantize_ref(qa.codes, qa.scales)
-    db = dequantize_ref(qb.codes, qb.scales)
+    da = dequantize_ref(qa.codes, qa.scales, qa.fmt)
+    db = dequantize_ref(qb.codes, qb.scales, qb.fmt)
     return da @ db.T
 
 
 def linear_ref(op: str, a_src: np.ndarray, b_src: np.ndarray, rotate: str = ROT_HADAMARD,
-               rounding: str = ROUND_RNE, seed: int = 0):
+               rounding: str = ROUND_RNE, seed: int = 0, fmt: str = FMT_FP4):
     """One GEMM of the triple ([36Kr] "Fehlerdiagnoseexperiment").
 
     fprop: a_src = X [T, in], b_src = W [out, in] -> Y [T, out] = X W^T
@@ -539,8 +650,8 @@ def linear_ref(op: str, a_src: np.ndarray, b_src: np.ndarray, rotate: str = ROT_
     axes = {"fprop": (1, 1), "dgrad": (1, 0), "wgrad": (0, 0)}[op]
     seed_a = seed & 0xFFFFFFFF
     seed_b = seed_a | (1 << 32)
-    qa = quantize_ref(a_src, axes[0], rotate=rotate, rounding=rounding, seed=seed_a)
-    qb = quantize_ref(b_src, axes[1], rotate=rotate, rounding=rounding, seed=seed_b)
+    qa = quantize_ref(a_src, axes[0], rotate=rotate, rounding=rounding, seed=seed_a, fmt=fmt)
+    qb = quantize_ref(b_src, axes[1], rotate=rotate, rounding=rounding, seed=seed_b, fmt=fmt)
     return mx_gemm_ref(qa, qb), qa, qb
 
 

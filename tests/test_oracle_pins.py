@@ -514,3 +514,152 @@ def test_tiled_layout_addresses_and_roundtrip():
         assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
         assert np.array_equal(oracle.untile_codes(tb, mn, k), codes)
         assert np.array_equal(oracle.untile_scales(sb, mn, k), scales)
+
+
+# ------------------------------------------------- E4M3 comparator (MXFP8)
+def _e4m3_torch_decode():
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_table_matches_torch():
+    """All 256 E4M3 codes decode as torch's float8_e4m3fn does (bias 7,
+    subnormals at exponent 0, NaN only at S.1111.111, largest finite 448)."""
+    want = _e4m3_torch_decode()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert np.all(np.diff(oracle.e4m3_magnitudes()) > 0)
+
+
+def test_e4m3_rne_matches_torch_and_brute_force():
+    """Round to nearest even: torch's fp32 -> float8_e4m3fn conversion on
+    every midpoint, its fp32 neighbours and random values below 464 (torch
+    rounds 448..464 down to 448 like the saturating rule); a brute-force
+    nearest search decides the non-ties."""
+    torch = pytest.importorskip("torch")
+    g = oracle.e4m3_magnitudes()
+    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(21)
+    vals = np.concatenate([
+        g.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+        np.nextafter(mids, np.float32(1e9)),
+        (rng.random(200000) * 463.9).astype(np.float32),
+        (2.0 ** rng.uniform(-14, 8.8, 200000)).astype(np.float32)])
+    vals = vals[vals < 464]
+    got = oracle.round_e4m3_rne(vals)
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    # brute force: a non-tie goes to the strictly nearest magnitude
+    v64 = vals.astype(np.float64)[:5000]
+    d = np.abs(v64[:, None] - g[None, :])
+    best = np.argmin(d, axis=1)
+    srt = np.sort(d, axis=1)
+    clear = srt[:, 0] < srt[:, 1]
+    assert np.array_equal(got[:5000][clear], best[clear])
+
+
+def test_e4m3_saturates_at_448():
+    """Scaled values t in [448, 512) (possible since 2^-e * amax < 2^9) take
+    the largest finite code 0x7E, never the NaN code."""
+    for v in (448.0, 448.5, 463.9, 464.0, 480.0, 511.99):
+        assert oracle.round_e4m3_rne(np.array([v], np.float32))[0] == 0x7E
+
+
+def test_e4m3_one_hot_block():
+    """H32 of a one-hot block: every y = +-c, c = 0.17677669; floor(log2 c) =
+    -3 -> e = -3 - 8 = -11 (scale code 116); t = c * 2^11 = 362.04, between
+    352 and 384 -> 352 = 1.375 * 2^8 (code 0x7B); dequantized 0.171875."""
+    H = oracle.sylvester_hadamard(32)
+    for j in (0, 9, 31):
+        x = np.zeros((1, 32), np.float32)
+        x[0, j] = 1.0
+        q = oracle.quantize_ref(_bf16(x), axis=1, rotate="hadamard", fmt="fp8_e4m3")
+        assert q.scales[0, 0] == 116
+        assert np.array_equal(q.codes[0], np.where(H[:, j] > 0, 0x7B, 0xFB))
+        d = oracle.dequantize_ref(q.codes, q.scales, "fp8_e4m3")[0]
+        assert np.allclose(np.abs(d), 0.171875)
+
+
+def test_e4m3_constant_zero_and_nan_blocks():
+    """x = 1 without rotation: e = 0 - 8 (scale 119), t = 256 -> code 0x78.
+    A zero block takes scale code 0 and zero codes; a NaN block scale 0xFF."""
+    x = np.zeros((3, 64), np.float32)
+    x[0, :32] = 1.0
+    x[2, 33] = np.nan
+    q = oracle.quantize_ref(_bf16(x), axis=1, rotate="none", fmt="fp8_e4m3")
+    assert q.scales[0, 0] == 119 and np.all(q.codes[0, :32] == 0x78)
+    assert q.scales[1, 0] == 0 and np.all(q.codes[1] == 0)
+    assert q.scales[2, 1] == 0xFF and np.all(q.codes[2, 32:] == 0)
+    with pytest.raises(ValueError):
+        oracle.quantize_ref(_bf16(x), axis=1, rounding="sr", fmt="fp8_e4m3")
+
+
+def test_e4m3_requantizing_representable_block_is_fixed_point():
+    rng = np.random.default_rng(22)
+    for trial in range(400):
+        s = int(rng.integers(10, 240))
+        codes = rng.integers(0, 256, 32).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0
+        codes[rng.integers(0, 32)] = rng.integers(0x78, 0x7F) | (rng.integers(0, 2) << 7)
+        d = oracle.dequantize_ref(codes[None], np.array([[s]], np.uint8), "fp8_e4m3")
+        x = _bf16(d.astype(np.float32))
+        assert np.array_equal(bf16_bits_to_f32(x).astype(np.float64), d)
+        q = oracle.quantize_ref(x, axis=1, rotate="none", fmt="fp8_e4m3")
+        assert q.scales[0, 0] == s
+        # -0 codes come back as +0 only where the input bf16 was +0
+        assert np.array_equal(q.codes[0] & 0x7F, codes & 0x7F)
+        nz = (codes & 0x7F) != 0
+        assert np.array_equal(q.codes[0][nz], codes[nz])
+
+
+def test_e4m3_gemm_matches_exact_fractions():
+    rng = np.random.default_rng(23)
+    a = f32_to_bf16_bits(rng.standard_normal((9, 64)).astype(np.float32))
+    b = f32_to_bf16_bits(rng.standard_normal((7, 64)).astype(np.float32))
+    qa = oracle.quantize_ref(a, 1, fmt="fp8_e4m3")
+    qb = oracle.quantize_ref(b, 1, fmt="fp8_e4m3")
+    C = oracle.mx_gemm_ref(qa, qb)
+    for m in range(9):
+        for n in range(7):
+            acc = Fraction(0)
+            for k in range(64):
+                va = Fraction(oracle.e4m3_value(int(qa.codes[m, k]))) * \
+                    Fraction(2) ** (int(qa.scales[m, k // 32]) - 127)
+                vb = Fraction(oracle.e4m3_value(int(qb.codes[n, k]))) * \
+                    Fraction(2) ** (int(qb.scales[n, k // 32]) - 127)
+                acc += va * vb
+            assert C[m, n] == float(acc)
+
+
+def test_e4m3_linear_error_is_below_e2m1():
+    """With three mantissa bits instead of one the MXFP8 product of the same
+    operands sits far closer to the exact product than the MXFP4 one."""
+    rng = np.random.default_rng(24)
+    X = f32_to_bf16_bits(rng.standard_normal((64, 128)).astype(np.float32))
+    W = f32_to_bf16_bits(rng.standard_normal((48, 128)).astype(np.float32))
+    exact = bf16_bits_to_f32(X).astype(np.float64) @ bf16_bits_to_f32(W).astype(np.float64).T
+    for rot in ("hadamard", "none"):
+        c8, _, _ = oracle.linear_ref("fprop", X, W, rotate=rot, fmt="fp8_e4m3")
+        c4, _, _ = oracle.linear_ref("fprop", X, W, rotate=rot)
+        e8 = np.linalg.norm(c8 - exact) / np.linalg.norm(exact)
+        e4 = np.linalg.norm(c4 - exact) / np.linalg.norm(exact)
+        assert e8 < 0.05 and e8 < e4 / 3, (rot, e8, e4)
+
+
+def test_e4m3_tiled_layout_addresses_and_roundtrip():
+    rng = np.random.default_rng(25)
+    for mn, k in ((37, 160), (16, 128), (300, 64)):
+        codes = rng.integers(0, 256, (mn, k)).astype(np.uint8)
+        tb = oracle.tile_codes_fp8(codes)
+        mnp, kp = oracle.padded_extents(mn, k)
+        assert tb.size == mnp * kp
+        for m in range(mn):
+            for kk in range(0, k, 5):
+                g, r, q, c = m // 16, m % 16, kk // 128, (kk % 128) // 32
+                assert tb[(g * (kp // 128) + q) * 2048 + c * 512 + r * 32 + kk % 32] == codes[m, kk]
+        full = oracle.untile_codes_fp8(tb, mnp, kp)
+        assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
+        assert np.array_equal(oracle.untile_codes_fp8(tb, mn, k), codes)
