@@ -30,13 +30,17 @@ if ROOT not in sys.path:
 
 METRIC = "MXFP4 linear TFLOP/s incl. Hadamard+quant, Llama-3.1-8B shapes; % MFMA peak"
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense MXFP8 MFMA (the E4M3 comparator)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 GEMM_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm.hip"
+GEMM_E4M3_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm_e4m3.hip"
 WORKLOADS_REF = None
 GEMM_TRAFFIC = "profiles/gemm_{}_traffic.md"
+GEMM_E4M3_TRAFFIC = "profiles/gemm_e4m3_{}_traffic.md"
 QUANT_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_quant.hip"
 QUANT_TRAFFIC = "profiles/quant_{}_traffic.md"
+QUANT_E4M3_TRAFFIC = "profiles/quant_e4m3_{}_traffic.md"
 
 
 def parse():
@@ -46,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fprop_q_proj")
     ap.add_argument("--variant", default=None)
+    ap.add_argument("--format", default="fp4_e2m1", choices=("fp4_e2m1", "fp8_e4m3"),
+                    help="element format of the timed path (fp8_e4m3: the MXFP8 comparator)")
     ap.add_argument("--all", action="store_true",
                     help="also time every other workload/variant and the full block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -63,13 +69,17 @@ class Runner:
     """Pre-marshalled C-ABI calls for one workload variant (no torch calls in
     the timed loop)."""
 
-    def __init__(self, mx, w, variant, tensors=None, min_bytes=2 * LLC_BYTES, device="cuda"):
+    def __init__(self, mx, w, variant, tensors=None, min_bytes=2 * LLC_BYTES, device="cuda",
+                 fmt="fp4_e2m1"):
         import numpy as np
         import torch
         from datagen import operands_for, workload_tensors
 
         self.w = w
+        self.fmt = fmt
         label, rot, rnd, seed = [v for v in w.variants if v[0] == variant][0]
+        if fmt == "fp8_e4m3" and rnd != "rne":
+            raise ValueError("the E4M3 comparator rounds to nearest only")
         self.variant, self.rot, self.rnd, self.seed = label, rot, rnd, seed
         t = tensors if tensors is not None else workload_tensors(w)
         a_src, self.ax_a, b_src, self.ax_b = operands_for(w, t)
@@ -92,16 +102,22 @@ class Runner:
         seed_a = seed & 0xFFFFFFFF
         seed_b = seed_a | (1 << 32)
         self.qa, self.qb, self.qcalls_a, self.qcalls_b = [], [], [], []
+        fp8 = fmt == "fp8_e4m3"
+        self.qfn = lib.mx_quantize_fp8 if fp8 else lib.mx_quantize
         for i in range(self.ncopy):
-            qa = mx.quantize(self.A[i], self.ax_a, rot, rnd, seed=seed_a)
-            qb = mx.quantize(self.B[i], self.ax_b, rot, rnd, seed=seed_b)
+            if fp8:
+                qa = mx.quantize_fp8(self.A[i], self.ax_a, rot, seed=seed_a)
+                qb = mx.quantize_fp8(self.B[i], self.ax_b, rot, seed=seed_b)
+            else:
+                qa = mx.quantize(self.A[i], self.ax_a, rot, rnd, seed=seed_a)
+                qb = mx.quantize(self.B[i], self.ax_b, rot, rnd, seed=seed_b)
             self.qa.append(qa)
             self.qb.append(qb)
             for q, src, lst in ((qa, self.A[i], self.qcalls_a), (qb, self.B[i], self.qcalls_b)):
                 r, c = src.shape
-                lst.append((src.data_ptr(), r, c, src.stride(0), q.desc.axis, 32,
-                            mx.ROTATE[rot], mx.ROUND[rnd], q.desc.seed, q.codes.data_ptr(),
-                            q.scales.data_ptr(), None, stream))
+                head = (src.data_ptr(), r, c, src.stride(0), q.desc.axis, 32, mx.ROTATE[rot])
+                tail = (q.desc.seed, q.codes.data_ptr(), q.scales.data_ptr(), None, stream)
+                lst.append(head + tail if fp8 else head + (mx.ROUND[rnd],) + tail)
         self.M, self.N = self.qa[0].mn, self.qb[0].mn
         self.K = self.qa[0].k
         self.out_dtype = w.out_dtype
@@ -114,18 +130,17 @@ class Runner:
 
     def step(self, i):
         j = i % self.ncopy
-        lib = self.lib
-        if lib.mx_quantize(*self.qcalls_a[j]) or lib.mx_quantize(*self.qcalls_b[j]) or \
-                lib.mx_linear(*self.lcalls[j]):
+        if self.qfn(*self.qcalls_a[j]) or self.qfn(*self.qcalls_b[j]) or \
+                self.lib.mx_linear(*self.lcalls[j]):
             raise RuntimeError("library call failed")
 
     def quant_a(self, i):
-        if self.lib.mx_quantize(*self.qcalls_a[i % self.ncopy]):
-            raise RuntimeError("mx_quantize failed")
+        if self.qfn(*self.qcalls_a[i % self.ncopy]):
+            raise RuntimeError("quantize failed")
 
     def quant_b(self, i):
-        if self.lib.mx_quantize(*self.qcalls_b[i % self.ncopy]):
-            raise RuntimeError("mx_quantize failed")
+        if self.qfn(*self.qcalls_b[i % self.ncopy]):
+            raise RuntimeError("quantize failed")
 
     def gemm(self, i):
         if self.lib.mx_linear(*self.lcalls[i % self.ncopy]):
@@ -135,13 +150,16 @@ class Runner:
     def flops(self):
         return 2.0 * self.M * self.N * self.K
 
+    def code_bytes(self):
+        return 1.0 if self.fmt == "fp8_e4m3" else 0.5
+
     def quant_bytes(self, shape):
         n = shape[0] * shape[1]
-        return n * (2 + 0.5 + 1.0 / 32)
+        return n * (2 + self.code_bytes() + 1.0 / 32)
 
     def gemm_bytes(self):
         ob = 4 if self.out_dtype == "f32" else 2
-        return (self.M + self.N) * self.K * (0.5 + 1.0 / 32) + self.M * self.N * ob
+        return (self.M + self.N) * self.K * (self.code_bytes() + 1.0 / 32) + self.M * self.N * ob
 
 
 def time_loop(fn, iters, warmup):
@@ -214,9 +232,10 @@ def cpu_baseline(r, reps):
     t_q = t_g = 0.0
     for _ in range(reps):
         t0 = time.perf_counter()
-        qa = oracle.quantize_ref(r.a_src, r.ax_a, rotate=r.rot, rounding=r.rnd, seed=seed_a)
+        qa = oracle.quantize_ref(r.a_src, r.ax_a, rotate=r.rot, rounding=r.rnd, seed=seed_a,
+                                 fmt=r.fmt)
         qb = oracle.quantize_ref(r.b_src, r.ax_b, rotate=r.rot, rounding=r.rnd,
-                                 seed=seed_a | (1 << 32))
+                                 seed=seed_a | (1 << 32), fmt=r.fmt)
         t1 = time.perf_counter()
         oracle.mx_gemm_ref(qa, qb)
         t2 = time.perf_counter()
@@ -275,11 +294,15 @@ def main():
     w = WORKLOADS[args.workload]
     variant = args.variant or w.variants[0][0]
     print(f"[bench] workload {w.name} variant {variant}", file=sys.stderr, flush=True)
-    r = Runner(mx, w, variant)
+    fp8 = args.format == "fp8_e4m3"
+    r = Runner(mx, w, variant, fmt=args.format)
     res = measure(r, args.steps, args.warmup)
     t_dom = res["t_gemm_us"]
     gemm_ach = r.flops() / (t_dom * 1e-6) / 1e12
     qa_ach = res["quant_a_gbs"]
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_FP4_TFLOPS
+    gemm_src, gemm_prof = (GEMM_E4M3_SRC, GEMM_E4M3_TRAFFIC) if fp8 else (GEMM_SRC, GEMM_TRAFFIC)
+    quant_prof = QUANT_E4M3_TRAFFIC if fp8 else QUANT_TRAFFIC
     out = {
         "metric": METRIC,
         "value": round(res["tflops"], 2),
@@ -291,22 +314,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4_e2m1xfp4_e2m1->f32",
+        "dtype": "fp8_e4m3xfp8_e4m3->f32" if fp8 else "fp4_e2m1xfp4_e2m1->f32",
         "data": "synthetic (seeded PCG64; Llama-3.1-8B q_proj shapes, no real weights)",
         "config": {
             "workload": (f"{w.name}: {w.op} M={r.M} N={r.N} K={r.K}, rotate={r.rot}, "
                          f"round={r.rnd}, out={w.out_dtype}"),
             "M": r.M, "N": r.N, "K": r.K, "variant": variant, "input_copies": r.ncopy,
         },
-        "pct_mfma_peak": round(100.0 * res["tflops"] / PEAK_FP4_TFLOPS, 2),
+        "pct_mfma_peak": round(100.0 * res["tflops"] / peak, 2),
         "roofline": {
-            "kernel": "mx_gemm (MXFP4 MFMA GEMM)",
+            "kernel": ("gemm_e4m3_kernel (MXFP8 comparator GEMM)" if fp8
+                       else "gemm_tiled_kernel (MXFP4 MFMA GEMM)"),
             "bound": "mfma",
             "achieved": round(gemm_ach, 2),
-            "peak": PEAK_FP4_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(gemm_ach / PEAK_FP4_TFLOPS, 4),
-            "traffic": recorded_traffic(GEMM_SRC, GEMM_TRAFFIC.format(w.name)),
+            "frac": round(gemm_ach / peak, 4),
+            "traffic": recorded_traffic(gemm_src, gemm_prof.format(w.name)),
         },
         "quant_roofline": {
             "kernel": f"mx_quant axis {r.ax_a} (operand A)",
@@ -315,13 +339,16 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(qa_ach / PEAK_HBM_GBS, 4),
-            "traffic": recorded_traffic(QUANT_SRC, QUANT_TRAFFIC.format(w.name)),
+            "traffic": recorded_traffic(QUANT_SRC, quant_prof.format(w.name)),
         },
         "per_kernel_us": {k: round(res[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
                                                        "t_gemm_us")},
         "quant_b_gbs": round(res["quant_b_gbs"], 1),
         "gemm_only_tflops": round(res["gemm_tflops"], 2),
     }
+    if not fp8 and r.rnd == "rne":
+        out["fp8_comparator"] = fp8_comparator(mx, w, variant, max(10, args.steps // 2), res)
+        print(f"[bench] fp8 comparator {out['fp8_comparator']}", file=sys.stderr, flush=True)
     if args.all:
         extra = {}
         for name, wl in WORKLOADS.items():
@@ -360,6 +387,30 @@ def main():
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(r, args.cpu_reps)
     print(json.dumps(out), flush=True)
+
+
+def fp8_comparator(mx, w, variant, steps, fp4_res):
+    """The same workload and rotation through the MXFP8 (E4M3) comparator:
+    whole-step and per-kernel times beside the MXFP4 ones measured just
+    before, and the FP4 : FP8 speed ratios (the pages' context: FP4 has in
+    theory twice FP8's compute; the MXFP4 training step ran about 20% faster
+    than the FP8 baseline)."""
+    r8 = Runner(mx, w, variant, fmt="fp8_e4m3")
+    m8 = measure(r8, steps, 3)
+    fl = r8.flops()
+    out = {
+        "ms_per_step": round(m8["ms_per_step"], 5),
+        "tflops": round(m8["tflops"], 2),
+        "per_kernel_us": {k: round(m8[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
+                                                      "t_gemm_us")},
+        "gemm_tflops": round(fl / (m8["t_gemm_us"] * 1e-6) / 1e12, 2),
+        "gemm_frac_fp8_peak": round(fl / (m8["t_gemm_us"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "quant_a_gbs": round(m8["quant_a_gbs"], 1),
+        "fp4_over_fp8_step_speed": round(m8["ms_per_step"] / fp4_res["ms_per_step"], 3),
+        "fp4_over_fp8_gemm_speed": round(m8["t_gemm_us"] / fp4_res["t_gemm_us"], 3),
+    }
+    del r8
+    return out
 
 
 def output_mse(mx, wl, variants):

@@ -43,7 +43,7 @@ typedef enum mx_status {
   MX_ERR_SHAPE = -2,       /* bad extents: reduction extent % 32, ld < cols, K mismatch */
   MX_ERR_ALIGN = -3,       /* a device pointer or leading dimension is misaligned */
   MX_ERR_ARG = -4,         /* bad enum value, block != 32, axis wrong for the op  */
-  MX_ERR_MISMATCH = -5,    /* A and B were quantized with different rotations / sign seeds */
+  MX_ERR_MISMATCH = -5,    /* A and B quantized with different rotations / sign seeds / formats */
   MX_ERR_UNSUPPORTED = -6, /* valid request this build does not implement        */
   MX_ERR_HIP = -7          /* the HIP runtime reported a launch error            */
 } mx_status;
@@ -66,13 +66,25 @@ typedef enum mx_round {
   MX_ROUND_SR = 1     /* upper neighbour with probability (a-lo)/(hi-lo), 24-bit uniform */
 } mx_round;
 
+/* Element format of a quantized operand. MXFP4 is the method; MXFP8 with
+ * E4M3 elements is the baseline it is measured against (36Kr, opening
+ * section: FP4 has in theory twice FP8's compute; "Ende-zu-Ende-Effizienz":
+ * throughput against the FP8 baseline; ShowAPI page
+ * "AMD颠覆认知：FP4不稳定性的真正原因", section 2.2: E4M3 as an FP8 format). */
+typedef enum mx_format {
+  MX_FMT_FP4_E2M1 = 0,  /* written by mx_quantize / mx_quantize_dual           */
+  MX_FMT_FP8_E4M3 = 1   /* written by mx_quantize_fp8                         */
+} mx_format;
+
 typedef enum mx_op { MX_OP_FPROP = 0, MX_OP_DGRAD = 1, MX_OP_WGRAD = 2 } mx_op;
 
 typedef enum mx_out_dtype { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out_dtype;
 
 /*
- * A quantized operand, filled by mx_quantize. Its pointers are BORROWED from
- * the caller (the buffers passed to mx_quantize).
+ * A quantized operand, filled by mx_quantize (and mx_quantize_dual,
+ * mx_quantize_fp8). Its pointers are BORROWED from the caller (the buffers
+ * passed to the quantize call). The layout below is MXFP4's; the MXFP8
+ * comparator's codes are described at mx_quantize_fp8.
  *
  * The operand is always stored reduction-major ("K-major"), whatever the axis:
  *   MN = rows, K = cols   when axis == 1 (blocks run along a row);
@@ -110,6 +122,7 @@ typedef struct mx_qtensor {
   int32_t rotate;       /* mx_rotate used                                     */
   int32_t round;        /* mx_round used                                      */
   uint64_t seed;        /* seed used (see mx_quantize)                        */
+  int32_t format;       /* mx_format of the codes (layout: see mx_quantize_fp8) */
 } mx_qtensor;
 
 /*
@@ -183,8 +196,45 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
                            void *scales0, mx_qtensor *desc1, mx_qtensor *desc0, void *stream);
 
 /*
+ * Byte sizes of the tiled codes and scales of mx_quantize_fp8 (codes: one
+ * byte per element, MNp * Kp; scales as for MXFP4, MNp * Kp / 32). Host-only.
+ * Errors as for mx_quantize_sizes.
+ */
+mx_status mx_quantize_fp8_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
+                                size_t *codes_bytes, size_t *scales_bytes);
+
+/*
+ * Rotate + quantize a bf16 tensor into MXFP8 with E4M3 elements: the FP8
+ * comparator of the MXFP4 path (see mx_format). Same blocks, rotations and
+ * E8M0 scales as mx_quantize; the block exponent is floor(log2 amax) - 8
+ * (E4M3's largest exponent), clamped to [-127, 127], and each element
+ * t = y * 2^-e is rounded to the nearest E4M3 value, ties to even, values
+ * above 448 saturating to 448. Only nearest rounding: the pages compare
+ * stochastic rounding within MXFP4, not within FP8.
+ *
+ *  x_bf16, rows, cols, ld, axis, block, rotate, seed, out_desc, stream:
+ *          as for mx_quantize (seed only feeds the random signs).
+ *  codes   device, >= codes_bytes of mx_quantize_fp8_sizes, 16-byte aligned.
+ *          Same zero-padded [MNp, Kp] extent and 16 x 128 tiles as MXFP4, but
+ *          a tile is 2 KB, at byte (g * Kp/128 + q) * 2048, holding
+ *          [16-element chunk j][row r][16 B]: K element k of the slice, row
+ *          r, at (k / 16) * 256 + r * 16 + k % 16. (The matrix instruction
+ *          takes lane (r, g)'s 32 bytes as chunks g and g + 4 of row r, i.e.
+ *          the 16 bytes at 16 l and at 1024 + 16 l for lane l = 16 g + r.)
+ *          Code = sign << 7 | E4M3 magnitude (exponent bias 7, 0x7E = 448;
+ *          0x7F is never written).
+ *  scales  as for mx_quantize.
+ * Limit: the padded codes (MNp * Kp bytes) must stay below 1 GiB.
+ * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_UNSUPPORTED,
+ * MX_ERR_HIP.
+ */
+mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                          int32_t axis, int32_t block, int32_t rotate, uint64_t seed,
+                          void *codes, void *scales, mx_qtensor *out_desc, void *stream);
+
+/*
  * One GEMM of the triple over two quantized operands, fp32 accumulation on
- * the gfx950 block-scaled FP4 matrix cores:
+ * the gfx950 block-scaled matrix cores:
  *     C[m][n] = sum_k A(m, k) * B(n, k)
  * with A, B in their tiled K-major form (36Kr, "Fehlerdiagnoseexperiment").
  *
@@ -198,6 +248,9 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
  * Both operands must use the same rotation and, for the random-sign rotation,
  * the same low 32 bits of the seed (else MX_ERR_MISMATCH): that is what makes
  * the rotation cancel in the product. Their reduction extents must match.
+ * Both must have the same format (else MX_ERR_MISMATCH): two MXFP8 operands
+ * run the E4M3 comparator GEMM (same call, same C), two MXFP4 operands the
+ * MXFP4 GEMM.
  * Requirements: C aligned to its element size (4 bytes for fp32, 2 for bf16),
  * ldc >= N. M or N == 0 launches nothing; K == 0 with M, N > 0 writes zeros.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN,

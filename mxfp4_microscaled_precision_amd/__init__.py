@@ -24,14 +24,15 @@ from typing import Optional, Tuple
 __all__ = [
     "LIB_PATH", "MxError", "QTensorDesc", "QTensor", "load_library", "library_symbols",
     "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "quantize_dual",
-    "linear",
-    "ROTATE", "ROUND", "OPS", "OUT_DTYPES", "OP_AXES",
+    "quantize_fp8_sizes", "quantize_fp8", "linear",
+    "ROTATE", "ROUND", "FORMATS", "OPS", "OUT_DTYPES", "OP_AXES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 ROTATE = {"none": 0, "hadamard": 1, "rand_sign_hadamard": 2, "hadamard16": 3}
 ROUND = {"rne": 0, "sr": 1}
+FORMATS = {"fp4_e2m1": 0, "fp8_e4m3": 1}
 OPS = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 OUT_DTYPES = {"f32": 0, "bf16": 1}
 # (A axis, B axis) each op needs
@@ -61,6 +62,7 @@ class QTensorDesc(ctypes.Structure):
         ("rotate", ctypes.c_int32),
         ("round", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
+        ("format", ctypes.c_int32),
     ]
 
 
@@ -70,6 +72,9 @@ _SIGNATURES = {
     "mx_quantize_sizes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "mx_quantize_fp8_sizes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_size_t)]),
     "mx_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
@@ -81,6 +86,11 @@ _SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.POINTER(QTensorDesc),
                                         ctypes.POINTER(QTensorDesc), ctypes.c_void_p]),
+    "mx_quantize_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.POINTER(QTensorDesc),
+                                       ctypes.c_void_p]),
     "mx_linear": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(QTensorDesc),
                                  ctypes.POINTER(QTensorDesc), ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_void_p]),
@@ -157,6 +167,13 @@ def quantize_sizes(rows: int, cols: int, axis: int, block: int = 32) -> Tuple[in
     return cb.value, sb.value
 
 
+def quantize_fp8_sizes(rows: int, cols: int, axis: int, block: int = 32) -> Tuple[int, int]:
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().mx_quantize_fp8_sizes(rows, cols, axis, block, ctypes.byref(cb),
+                                                ctypes.byref(sb)), "mx_quantize_fp8_sizes")
+    return cb.value, sb.value
+
+
 def _stream_handle(device, stream) -> int:
     import torch
     if stream is None:
@@ -183,12 +200,30 @@ class QTensor:
         return (self.desc.rows, self.desc.cols)
 
     @property
+    def format(self) -> str:
+        return {v: k for k, v in FORMATS.items()}[self.desc.format]
+
+    @property
     def mn(self) -> int:
         return self.desc.rows if self.desc.axis == 1 else self.desc.cols
 
     @property
     def k(self) -> int:
         return self.desc.cols if self.desc.axis == 1 else self.desc.rows
+
+
+def _source_extents(x) -> Tuple[int, int, int]:
+    """(rows, cols, ld) of a 2-D bf16 CUDA source; raises for anything else."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be a CUDA (HIP) tensor; there is no CPU path")
+    if x.numel() > 0 and x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else max(cols, 8 * ((cols + 7) // 8))
+    return rows, cols, ld
 
 
 def quantize(x, axis: int, rotate: str = "hadamard", round: str = "rne", seed: int = 0,
@@ -200,14 +235,7 @@ def quantize(x, axis: int, rotate: str = "hadamard", round: str = "rne", seed: i
     """
     import torch
     lib = load_library()
-    if x.dim() != 2 or x.dtype != torch.bfloat16:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
-    if not x.is_cuda:
-        raise ValueError("x must be a CUDA (HIP) tensor; there is no CPU path")
-    if x.numel() > 0 and x.stride(1) != 1:
-        raise ValueError("x must have unit column stride")
-    rows, cols = x.shape
-    ld = x.stride(0) if rows > 1 else max(cols, 8 * ((cols + 7) // 8))
+    rows, cols, ld = _source_extents(x)
     cb, sb = quantize_sizes(rows, cols, axis)
     if codes is None:
         codes = torch.empty((cb,), dtype=torch.uint8, device=x.device)
@@ -231,14 +259,7 @@ def quantize_dual(x, rotate: str = "hadamard", round: str = "rne", seed1: int = 
     mx_quantize_dual): returns (axis-1 operand, axis-0 operand)."""
     import torch
     lib = load_library()
-    if x.dim() != 2 or x.dtype != torch.bfloat16:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
-    if not x.is_cuda:
-        raise ValueError("x must be a CUDA (HIP) tensor; there is no CPU path")
-    if x.numel() > 0 and x.stride(1) != 1:
-        raise ValueError("x must have unit column stride")
-    rows, cols = x.shape
-    ld = x.stride(0) if rows > 1 else max(cols, 8 * ((cols + 7) // 8))
+    rows, cols, ld = _source_extents(x)
     out = []
     for axis in (1, 0):
         cb, sb = quantize_sizes(rows, cols, axis)
@@ -255,9 +276,34 @@ def quantize_dual(x, rotate: str = "hadamard", round: str = "rne", seed1: int = 
     return QTensor(c1, s1, d1), QTensor(c0, s0, d0)
 
 
+def quantize_fp8(x, axis: int, rotate: str = "hadamard", seed: int = 0, codes=None,
+                 scales=None, stream=None) -> QTensor:
+    """Rotate + quantize into MXFP8 with E4M3 elements, the FP8 comparator
+    (see mx_quantize_fp8; nearest rounding only). Arguments as for quantize."""
+    import torch
+    lib = load_library()
+    rows, cols, ld = _source_extents(x)
+    cb, sb = quantize_fp8_sizes(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty((cb,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((sb,), dtype=torch.uint8, device=x.device)
+    if codes.numel() < cb or scales.numel() < sb:
+        raise ValueError("codes / scales buffers too small")
+    desc = QTensorDesc()
+    st = lib.mx_quantize_fp8(x.data_ptr() if x.numel() else None, rows, cols, ld, axis, 32,
+                             ROTATE[rotate], seed & 0xFFFFFFFFFFFFFFFF,
+                             codes.data_ptr() if codes.numel() else None,
+                             scales.data_ptr() if scales.numel() else None,
+                             ctypes.byref(desc), _stream_handle(x.device, stream))
+    _check(st, "mx_quantize_fp8")
+    return QTensor(codes, scales, desc)
+
+
 def linear(op: str, A: QTensor, B: QTensor, out_dtype: str = "f32", out=None,
            stream=None):
-    """One GEMM of the triple (see mx_linear); returns C [M, N] (fp32 or bf16)."""
+    """One GEMM of the triple (see mx_linear); returns C [M, N] (fp32 or bf16).
+    Two MXFP8 operands (quantize_fp8) run the E4M3 comparator GEMM."""
     import torch
     lib = load_library()
     M, N = A.mn, B.mn

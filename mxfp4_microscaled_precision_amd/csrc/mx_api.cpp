@@ -1,4 +1,5 @@
-// C ABI of the MXFP4 library: argument validation and launch dispatch.
+// C ABI of the MXFP4 library (and its MXFP8 comparator): argument validation
+// and launch dispatch.
 // Every check runs on the host before anything is enqueued, so an invalid
 // call launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
@@ -25,6 +26,10 @@ bool valid_rotate(int32_t r) {
          r == MX_ROT_HADAMARD16;
 }
 bool valid_round(int32_t r) { return r == MX_ROUND_RNE || r == MX_ROUND_SR; }
+bool valid_format(int32_t f) { return f == MX_FMT_FP4_E2M1 || f == MX_FMT_FP8_E4M3; }
+
+// Code bytes per element, times two (E2M1: half a byte; E4M3: one byte).
+int64_t code_bytes_x2(int32_t format) { return format == MX_FMT_FP8_E4M3 ? 2 : 1; }
 
 // Reduction (K) and non-reduction (MN) extents of a quantized operand.
 void operand_extents(const mx_qtensor *q, int64_t *mn, int64_t *k) {
@@ -37,7 +42,7 @@ void operand_extents(const mx_qtensor *q, int64_t *mn, int64_t *k) {
   }
 }
 
-// Tiled-layout extents: MN up to a multiple of 16, K up to a multiple of 128
+// Tiled-layout extents: MN up to a multiple of 256, K up to a multiple of 128
 // (empty operands stay empty).
 void padded_extents(int64_t rows, int64_t cols, int32_t axis, int64_t *mnp, int64_t *kp) {
   const int64_t mn = axis == 1 ? rows : cols;
@@ -56,6 +61,8 @@ mx_status check_qtensor(const mx_qtensor *q) {
   if (q->axis != 0 && q->axis != 1) return MX_ERR_ARG;
   if (q->block != 32) return MX_ERR_ARG;
   if (!valid_rotate(q->rotate) || !valid_round(q->round)) return MX_ERR_ARG;
+  if (!valid_format(q->format)) return MX_ERR_ARG;
+  if (q->format == MX_FMT_FP8_E4M3 && q->round != MX_ROUND_RNE) return MX_ERR_ARG;
   if (q->rows < 0 || q->cols < 0) return MX_ERR_SHAPE;
   const int64_t k = q->axis == 1 ? q->cols : q->rows;
   if (k % 32 != 0) return MX_ERR_SHAPE;
@@ -64,17 +71,54 @@ mx_status check_qtensor(const mx_qtensor *q) {
     if (!aligned(q->codes, 16) || !aligned(q->scales, 4)) return MX_ERR_ALIGN;
     int64_t mnp, kp;
     padded_extents(q->rows, q->cols, q->axis, &mnp, &kp);
-    if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
+    if (mnp * kp * code_bytes_x2(q->format) / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
   }
   return MX_OK;
 }
 
-}  // namespace
+void fill_desc(mx_qtensor *d, void *codes, void *scales, int64_t rows, int64_t cols,
+               int32_t axis, int32_t block, int32_t rotate, int32_t round, uint64_t seed,
+               int32_t format) {
+  if (d == nullptr) return;
+  d->codes = codes;
+  d->scales = scales;
+  d->rows = rows;
+  d->cols = cols;
+  d->axis = axis;
+  d->block = block;
+  d->rotate = rotate;
+  d->round = round;
+  d->seed = seed;
+  d->format = format;
+}
 
-extern "C" {
+// Validation shared by the single-orientation quantize calls.
+mx_status check_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                         int32_t axis, int32_t block, int32_t rotate, int32_t round,
+                         const void *codes, const void *scales, int32_t format) {
+  if (axis != 0 && axis != 1) return MX_ERR_ARG;
+  if (block != 32) return MX_ERR_ARG;
+  if (!valid_rotate(rotate) || !valid_round(round)) return MX_ERR_ARG;
+  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+  const int64_t k = axis == 1 ? cols : rows;
+  if (k % 32 != 0) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return MX_ERR_NULL;
+  if (ld < cols) return MX_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
+  int64_t mnp, kp;
+  padded_extents(rows, cols, axis, &mnp, &kp);
+  if (mnp * kp * code_bytes_x2(format) / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
+  if (axis == 1) {
+    if (ld % 8 != 0 || !aligned(x_bf16, 16)) return MX_ERR_ALIGN;
+  } else {
+    if (!aligned(x_bf16, 2)) return MX_ERR_ALIGN;
+  }
+  return MX_OK;
+}
 
-mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
-                            size_t *codes_bytes, size_t *scales_bytes) {
+mx_status sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block, int32_t format,
+                size_t *codes_bytes, size_t *scales_bytes) {
   if (codes_bytes == nullptr || scales_bytes == nullptr) return MX_ERR_NULL;
   if (axis != 0 && axis != 1) return MX_ERR_ARG;
   if (block != 32) return MX_ERR_ARG;
@@ -83,47 +127,19 @@ mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t bl
   if (k % 32 != 0) return MX_ERR_SHAPE;
   int64_t mnp, kp;
   padded_extents(rows, cols, axis, &mnp, &kp);
-  *codes_bytes = (size_t)mnp * (size_t)kp / 2;
+  *codes_bytes = (size_t)(mnp * kp * code_bytes_x2(format) / 2);
   *scales_bytes = (size_t)mnp * (size_t)kp / 32;
   return MX_OK;
 }
 
-mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld, int32_t axis,
-                      int32_t block, int32_t rotate, int32_t round, uint64_t seed, void *codes,
-                      void *scales, mx_qtensor *out_desc, void *stream) {
-  if (axis != 0 && axis != 1) return MX_ERR_ARG;
-  if (block != 32) return MX_ERR_ARG;
-  if (!valid_rotate(rotate) || !valid_round(round)) return MX_ERR_ARG;
-  if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
-  const int64_t k = axis == 1 ? cols : rows;
-  if (k % 32 != 0) return MX_ERR_SHAPE;
-  const bool empty = rows == 0 || cols == 0;
-  if (!empty) {
-    if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return MX_ERR_NULL;
-    if (ld < cols) return MX_ERR_SHAPE;
-    if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
-    int64_t mnp, kp;
-    padded_extents(rows, cols, axis, &mnp, &kp);
-    if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
-    if (axis == 1) {
-      if (ld % 8 != 0 || !aligned(x_bf16, 16)) return MX_ERR_ALIGN;
-    } else {
-      if (!aligned(x_bf16, 2)) return MX_ERR_ALIGN;
-    }
-  }
-  if (out_desc != nullptr) {
-    out_desc->codes = codes;
-    out_desc->scales = scales;
-    out_desc->rows = rows;
-    out_desc->cols = cols;
-    out_desc->axis = axis;
-    out_desc->block = block;
-    out_desc->rotate = rotate;
-    out_desc->round = round;
-    out_desc->seed = seed;
-  }
-  if (empty) return MX_OK;
-
+mx_status quantize_any(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld, int32_t axis,
+                       int32_t block, int32_t rotate, int32_t round, uint64_t seed, void *codes,
+                       void *scales, mx_qtensor *out_desc, void *stream, int32_t format) {
+  const mx_status st =
+      check_quantize(x_bf16, rows, cols, ld, axis, block, rotate, round, codes, scales, format);
+  if (st != MX_OK) return st;
+  fill_desc(out_desc, codes, scales, rows, cols, axis, block, rotate, round, seed, format);
+  if (rows == 0 || cols == 0) return MX_OK;
   mx::QuantArgs a;
   a.x = static_cast<const uint16_t *>(x_bf16);
   a.rows = rows;
@@ -137,7 +153,36 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
   a.codes = static_cast<uint8_t *>(codes);
   a.scales = static_cast<uint8_t *>(scales);
   a.rb = 0;
+  a.fmt = format == MX_FMT_FP8_E4M3 ? 1 : 0;
   return hip_status(mx::quantize_launch(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
+                            size_t *codes_bytes, size_t *scales_bytes) {
+  return sizes(rows, cols, axis, block, MX_FMT_FP4_E2M1, codes_bytes, scales_bytes);
+}
+
+mx_status mx_quantize_fp8_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
+                                size_t *codes_bytes, size_t *scales_bytes) {
+  return sizes(rows, cols, axis, block, MX_FMT_FP8_E4M3, codes_bytes, scales_bytes);
+}
+
+mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld, int32_t axis,
+                      int32_t block, int32_t rotate, int32_t round, uint64_t seed, void *codes,
+                      void *scales, mx_qtensor *out_desc, void *stream) {
+  return quantize_any(x_bf16, rows, cols, ld, axis, block, rotate, round, seed, codes, scales,
+                      out_desc, stream, MX_FMT_FP4_E2M1);
+}
+
+mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                          int32_t axis, int32_t block, int32_t rotate, uint64_t seed,
+                          void *codes, void *scales, mx_qtensor *out_desc, void *stream) {
+  return quantize_any(x_bf16, rows, cols, ld, axis, block, rotate, MX_ROUND_RNE, seed, codes,
+                      scales, out_desc, stream, MX_FMT_FP8_E4M3);
 }
 
 mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
@@ -164,21 +209,8 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
       if (mnp * kp / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
     }
   }
-  mx_qtensor *descs[2] = {desc0, desc1};
-  void *cs[2] = {codes0, codes1}, *ss[2] = {scales0, scales1};
-  const uint64_t seeds[2] = {seed0, seed1};
-  for (int axis = 0; axis < 2; ++axis) {
-    if (descs[axis] == nullptr) continue;
-    descs[axis]->codes = cs[axis];
-    descs[axis]->scales = ss[axis];
-    descs[axis]->rows = rows;
-    descs[axis]->cols = cols;
-    descs[axis]->axis = axis;
-    descs[axis]->block = block;
-    descs[axis]->rotate = rotate;
-    descs[axis]->round = round;
-    descs[axis]->seed = seeds[axis];
-  }
+  fill_desc(desc0, codes0, scales0, rows, cols, 0, block, rotate, round, seed0, MX_FMT_FP4_E2M1);
+  fill_desc(desc1, codes1, scales1, rows, cols, 1, block, rotate, round, seed1, MX_FMT_FP4_E2M1);
   if (empty) return MX_OK;
 
   mx::DualArgs a;
@@ -210,7 +242,7 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
   // Which axis each operand must be quantized along, per op.
   static const int32_t need_axis[3][2] = {{1, 1}, {1, 0}, {0, 0}};
   if (A->axis != need_axis[op][0] || B->axis != need_axis[op][1]) return MX_ERR_ARG;
-  if (A->rotate != B->rotate) return MX_ERR_MISMATCH;
+  if (A->rotate != B->rotate || A->format != B->format) return MX_ERR_MISMATCH;
   if (A->rotate == MX_ROT_RAND_SIGN_HADAMARD &&
       (uint32_t)(A->seed & 0xFFFFFFFFull) != (uint32_t)(B->seed & 0xFFFFFFFFull))
     return MX_ERR_MISMATCH;
@@ -233,7 +265,9 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
   g.K = Ka;
   g.ldc = ldc;
   g.out_bf16 = out_dtype == MX_OUT_BF16 ? 1 : 0;
-  return hip_status(mx::gemm_launch(g, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(A->format == MX_FMT_FP8_E4M3 ? mx::gemm_e4m3_launch(g, s)
+                                                 : mx::gemm_launch(g, s));
 }
 
 const char *mx_status_string(int32_t status) {

@@ -24,15 +24,14 @@
 #include <atomic>
 #include <utility>
 
+#include "mx_gemm_common.h"
 #include "mx_kernels.h"
 
 namespace mx {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+using namespace gemm;
 
 constexpr int kFmtFp4 = 4;
 
@@ -47,62 +46,6 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, v4f c, u
                                                           (int)sa, SELB, (int)sb);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// Generic epilogue store of one quad: lane (lr, lg) of a 16x16 tile holds
-// C[row][col .. col + 3] with row = tile row + lr, col = tile col + 4 lg.
-// Element-wise and masked, for shapes the row-staged path does not take.
-template <int OUT_BF16>
-__device__ __forceinline__ void store_quad(const GemmArgs &g, const v4f &acc, int64_t row,
-                                           int64_t col) {
-  if (row >= g.M) return;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (col + r < g.N) {
-      if (OUT_BF16)
-        reinterpret_cast<uint16_t *>(g.c)[row * g.ldc + col + r] = f32_to_bf16_rne(acc[r]);
-      else
-        reinterpret_cast<float *>(g.c)[row * g.ldc + col + r] = acc[r];
-    }
-  }
-}
-
-// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
-// return zero.
-__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  v4i r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)(a >> 32);   // stride 0
-  r[2] = (int)bytes;                 // num_records in bytes
-  r[3] = 0x00020000;                 // raw buffer, 32-bit data format
-  return r;
-}
-
-// Direct-to-LDS loads: lane i's 16 (4) bytes from rsrc.base + voffset land at
-// LDS byte address lds_base + 16 i (4 i). Written as inline asm so that the
-// compiler neither serialises consecutive DMA loads nor waits for them before
-// unrelated LDS reads (it cannot tell LDS destinations apart); the kernel
-// waits for them explicitly (s_waitcnt vmcnt) before the barrier that
-// publishes a stage. The s_nop covers GFX9's one wait state between an M0
-// write and an LDS DMA that reads it.
-__device__ __forceinline__ void dma_load16(v4i rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :
-               : "v"(voffset), "s"(rsrc), "s"(lds_base)
-               : "memory", "m0");
-}
-
 // ---------------------------------------------------------------------------
 // 256x256 block tile. Twelve waves, three per SIMD: eight consumer waves in
 // a 2x4 grid, 128x64 each = 8x4 MFMA tiles (128 fp32 accumulators per lane),
@@ -113,19 +56,19 @@ __device__ __forceinline__ void dma_load4(v4i rsrc, int voffset, uint32_t lds_ba
 //
 // Operands are in the tiled layout the quantizer writes: a 1 KB tile holds 16
 // rows x 128 K elements as [32-block c][row r][16 B], which is exactly the
-// 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; scales of a
-// 128-wide K slice are one contiguous run of 4 bytes per row. K advances one
-// slice per stage through a ring of four LDS stage buffers with three stages
-// in flight. Every copy is a direct-to-LDS load of one contiguous span (a
-// 1 KB tile or 256 bytes of scales), and every LDS fragment read is one
-// contiguous 1 KB span, the only pattern gfx950's LDS serves at its full 256
-// bytes per clock (measured: a row-major layout takes 4x and an XOR-swizzled
-// one 2x the cycles; gathering rows from a row-major operand made the copies
-// 2.5x slower). Tiles past the operand's padded extent read as zero through
-// the buffer range check; padded rows and K blocks hold encoded zeros.
+// 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; the scales
+// of a 128-wide K slice and a 256-row panel are one contiguous 1 KB block in
+// which lane (r, c) finds the 16 row groups' bytes of row r, block c. K
+// advances one slice per stage through a ring of four LDS stage buffers with
+// three stages in flight. Every copy is a direct-to-LDS load of one
+// contiguous 1 KB span (a code tile or a scale block), and every LDS fragment
+// read is one contiguous 1 KB span, the only pattern gfx950's LDS serves at
+// its full 256 bytes per clock (measured: a row-major layout takes 4x and an
+// XOR-swizzled one 2x the cycles; gathering rows from a row-major operand
+// made the copies 2.5x slower). Tiles past the operand's padded extent read
+// as zero through the buffer range check; padded rows and K blocks hold
+// encoded zeros.
 // ---------------------------------------------------------------------------
-constexpr int kBM = 256;
-constexpr int kBN = 256;
 constexpr int kThreads = 768;                      // 8 consumer + 4 producer waves
 constexpr int kConsumers = 8;
 constexpr int kStageA = kBM * 64;                  // 16 tiles of 1 KB
@@ -135,46 +78,6 @@ constexpr int kStageSB = kBN * 4;
 constexpr int kStageBytes = kStageA + kStageB + kStageSA + kStageSB;
 constexpr int kRing = 4;                           // stage buffers (136 KB)
 constexpr int kAhead = kRing - 1;                  // stages in flight
-constexpr int kGroupM = 8;                         // tile rows per ordering group
-
-// Tile index -> (tile_m, tile_n): workgroups are dispatched round-robin over
-// the 8 XCDs, so consecutive ids are first regrouped per XCD, then ordered in
-// groups of kGroupM tile rows so that each XCD works on a compact 2-D region
-// of C and shares its A and B panels through its own L2.
-__device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int *mi, int *ni) {
-  const int T = tm * tn;
-  int id = bid;
-  if ((T & 7) == 0) id = (bid & 7) * (T >> 3) + (bid >> 3);
-  const int per_group = kGroupM * tn;
-  const int grp = id / per_group;
-  const int first_m = grp * kGroupM;
-  const int gm = min(kGroupM, tm - first_m);
-  const int r = id - grp * per_group;
-  *mi = first_m + r % gm;
-  *ni = r / gm;
-}
-
-// One finished quad: lane (lr, lg) of a 16x16 tile holds C[row][col .. col + 3]
-// (B is the MFMA's first operand). One 8-byte (bf16) or 16-byte (fp32)
-// store when the address allows it, else element-wise.
-template <int OUT_BF16>
-__device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc, int64_t row,
-                                               int64_t col, bool vec_ok) {
-  if (row >= g.M) return;
-  if (vec_ok && col + 3 < g.N) {
-    if (OUT_BF16) {
-      uint2 v;
-      v.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-      v.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col) = v;
-    } else {
-      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col) =
-          make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-  } else {
-    store_quad<OUT_BF16>(g, acc, row, col);
-  }
-}
 
 // Row I of a consumer's stage: read A fragment I + 1, then the 4 MFMAs of
 // row I (reading two rows ahead was measured slower on Wgrad and Dgrad). B is the first MFMA operand (its scale byte j of sb), A the second

@@ -1,0 +1,114 @@
+// Pieces shared by the gfx950 GEMM kernels (MXFP4 and the MXFP8 comparator):
+// vector types, the bf16 epilogue conversion and stores, raw buffer
+// resources with direct-to-LDS loads, and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_kernels.h"
+
+namespace mx {
+namespace gemm {
+
+constexpr int kBM = 256;                           // block tile rows (A)
+constexpr int kBN = 256;                           // block tile columns (B)
+constexpr int kGroupM = 8;                         // tile rows per ordering group
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Generic epilogue store of one quad: lane (lr, lg) of a 16x16 tile holds
+// C[row][col .. col + 3] with row = tile row + lr, col = tile col + 4 lg.
+// Element-wise and masked, for shapes the row-staged path does not take.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_quad(const GemmArgs &g, const v4f &acc, int64_t row,
+                                           int64_t col) {
+  if (row >= g.M) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (col + r < g.N) {
+      if (OUT_BF16)
+        reinterpret_cast<uint16_t *>(g.c)[row * g.ldc + col + r] = f32_to_bf16_rne(acc[r]);
+      else
+        reinterpret_cast<float *>(g.c)[row * g.ldc + col + r] = acc[r];
+    }
+  }
+}
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero.
+__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);   // stride 0
+  r[2] = (int)bytes;                 // num_records in bytes
+  r[3] = 0x00020000;                 // raw buffer, 32-bit data format
+  return r;
+}
+
+// Direct-to-LDS load: lane i's 16 bytes from rsrc.base + voffset land at LDS
+// byte address lds_base + 16 i. Written as inline asm so that the
+// compiler neither serialises consecutive DMA loads nor waits for them before
+// unrelated LDS reads (it cannot tell LDS destinations apart); the kernel
+// waits for them explicitly (s_waitcnt vmcnt) before the barrier that
+// publishes a stage. The s_nop covers GFX9's one wait state between an M0
+// write and an LDS DMA that reads it.
+__device__ __forceinline__ void dma_load16(v4i rsrc, int voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voffset), "s"(rsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+
+// Tile index -> (tile_m, tile_n): workgroups are dispatched round-robin over
+// the 8 XCDs, so consecutive ids are first regrouped per XCD, then ordered in
+// groups of kGroupM tile rows so that each XCD works on a compact 2-D region
+// of C and shares its A and B panels through its own L2.
+__device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int *mi, int *ni) {
+  const int T = tm * tn;
+  int id = bid;
+  if ((T & 7) == 0) id = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int per_group = kGroupM * tn;
+  const int grp = id / per_group;
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, tm - first_m);
+  const int r = id - grp * per_group;
+  *mi = first_m + r % gm;
+  *ni = r / gm;
+}
+
+// One finished quad: lane (lr, lg) of a 16x16 tile holds C[row][col .. col + 3]
+// (B is the MFMA's first operand). One 8-byte (bf16) or 16-byte (fp32)
+// store when the address allows it, else element-wise.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc, int64_t row,
+                                               int64_t col, bool vec_ok) {
+  if (row >= g.M) return;
+  if (vec_ok && col + 3 < g.N) {
+    if (OUT_BF16) {
+      uint2 v;
+      v.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+      v.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col) = v;
+    } else {
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  } else {
+    store_quad<OUT_BF16>(g, acc, row, col);
+  }
+}
+
+}  // namespace gemm
+}  // namespace mx

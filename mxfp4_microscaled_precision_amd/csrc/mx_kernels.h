@@ -35,9 +35,10 @@ struct QuantArgs {
   int axis;            // 0 or 1
   int rotate, round;
   uint32_t seed_lo, seed_hi;
-  uint8_t *codes;      // K-major packed codes
-  uint8_t *scales;     // K-major scales
+  uint8_t *codes;      // tiled codes
+  uint8_t *scales;     // tiled scales
   int rb;              // axis-0 row blocks per lane (0 = default)
+  int fmt;             // 0: E2M1 (MXFP4), 1: E4M3 (MXFP8 comparator, RNE only)
 };
 
 hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream);
@@ -64,5 +65,12 @@ struct GemmArgs {
 };
 
 hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream);
+
+// The MXFP8 (E4M3) comparator GEMM on the same tiled operands (2 KB code
+// tiles); same arguments.
+hipError_t gemm_e4m3_launch(const GemmArgs &g, hipStream_t stream);
+
+// Compute units of the current device (one persistent GEMM workgroup each).
+int cu_count();
 
 }  // namespace mx

@@ -67,6 +67,12 @@ __device__ __forceinline__ void butterfly16x2(float (&y)[32]) {
   }
 }
 
+// Element formats: the E2M1 elements of MXFP4, and the E4M3 elements of the
+// MXFP8 comparator (same 32-element blocks and E8M0 scales; one code byte per
+// element; nearest-even rounding only).
+constexpr int kFmtE2M1 = 0;
+constexpr int kFmtE4M3 = 1;
+
 // Rotation kind of the encoder: 0 none, 1 the 32-point Hadamard (with or
 // without random signs), 2 the 16-point variant.
 template <int ROT>
@@ -95,18 +101,29 @@ __device__ __forceinline__ float rot_norm() {
 //
 //  * amax: max |y| = fl32(max |h| * c), since rounding is monotonic; a NaN
 //    or Inf anywhere in the block marks it (see the amax comment below).
-//  * scale: e from amax; t = fl32(y * 2^-e). For e <= 123, c_e = c * 2^-e is
-//    an exact normal fp32 number and t = fl32(h * c_e) equals fl32(y * 2^-e)
-//    bit for bit (a power-of-two scaling commutes with rounding unless t is
-//    subnormal, and a subnormal t encodes as a signed zero either way). For
-//    e > 123 the two multiplies are done as written.
+//  * scale: e from amax; t = fl32(y * 2^-e). Stochastic rounding reads
+//    every bit of t, so it takes the two multiplies as written. For nearest
+//    rounding with e <= 123, c_e = c * 2^-e is an exact normal fp32 number
+//    and t = fl32(h * c_e) gives the same code as fl32(y * 2^-e): a
+//    power-of-two scaling commutes with rounding unless y or t is subnormal.
+//    A subnormal t encodes as a signed zero either way. A subnormal y needs
+//    |h| < 2^-123.5, and h is then n * 2^-133 with n < 724 (bf16's finest
+//    step; butterfly sums of such values are exact); no such n * c comes
+//    within fp32 rounding distance of a decision threshold times 2^e (the
+//    thresholds are multiples of 2^-10: it would need |16 c n - j| < 2^-13
+//    for an integer j, and over n < 724 the closest approach is 8.8e-4, at
+//    n = 204).
+//    For e > 123 the two multiplies are done as written.
 //  * RNE: v_cvt_scalef32_pk_fp4_f32 at scale 1.0, which rounds to nearest
 //    even and saturates at +-6 exactly like the threshold rule (checked over
 //    every fp32 pattern); two elements per instruction, element 2j in the low
-//    nibble. SR: integer rule of e2m1_sr_mag with the Philox uniform.
-template <int RK, int RND, typename U24Fn>
-__device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_t (&out)[4],
+//    nibble. SR: integer rule of e2m1_sr_mag with the Philox uniform. E4M3
+//    (nearest only): e4m3_rne, one code byte per element.
+template <int RK, int RND, int FMT, typename U24Fn>
+__device__ __forceinline__ uint32_t quantize_block(const float (&v)[32],
+                                                   uint32_t (&out)[FMT == kFmtE4M3 ? 8 : 4],
                                                    U24Fn u24_of) {
+  constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
   // amax as bits of |v| (a NaN or Inf compares above 0x7f800000). Without
   // the 32-point rotation: integer max of |bits|, which sees a lone NaN (the
   // 16-point variant leaves one half finite when the other holds a NaN).
@@ -126,12 +143,17 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
   const bool nonfinite = amax >= 0x7F800000u;
   const float c = rot_norm<RK>();
   if (RK) amax = f_bits(__fmul_rn(bits_f(amax), c));
-  const int e = block_exponent(amax);
+  // E4M3's largest exponent is 8 where E2M1's is 2: six more below the amax
+  const int e = FMT == kFmtE4M3 ? max(block_exponent(amax) - 6, -127) : block_exponent(amax);
   float t[32];
   if (!RK) {
     const float p = pow2_neg(e);
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], p);
+  } else if (RND == MX_K_ROUND_SR) {
+    const float p = pow2_neg(e);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], c), p);
   } else if (__builtin_expect(!__any(e > 123), 1)) {
     // c * 2^-e is an exact normal number for e <= 123: one multiply gives
     // the bits of fl32(fl32(h * c) * 2^-e)
@@ -146,7 +168,12 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], m1), m2);
   }
-  if (RND == MX_K_ROUND_SR) {
+  if constexpr (FMT == kFmtE4M3) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      out[j] = e4m3_rne(t[4 * j]) | (e4m3_rne(t[4 * j + 1]) << 8) |
+               (e4m3_rne(t[4 * j + 2]) << 16) | (e4m3_rne(t[4 * j + 3]) << 24);
+  } else if (RND == MX_K_ROUND_SR) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = 0u;
 #pragma unroll
@@ -168,17 +195,16 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32], uint32_
   }
   if (nonfinite) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = 0u;
+    for (int j = 0; j < kWords; ++j) out[j] = 0u;
     return 0xFFu;
   }
   return (uint32_t)(e + 127);
 }
 
-// Scale of one block for the two-multiply form t = fl32(fl32(v * m1) * m2):
-// m1 = c * 2^-e, m2 = 1 when that product is an exact normal number (e <=
-// 123), else m1 = c, m2 = 2^-e (with rotation); m1 = 2^-e, m2 = 1 without.
-// Returns the scale code (0xFF for a block holding a NaN or Inf, detected as
-// in quantize_block).
+// Scale of one block for stochastic rounding, t = fl32(fl32(v * m1) * m2):
+// m1 = c, m2 = 2^-e with rotation (the two roundings as defined, see
+// quantize_block); m1 = 2^-e, m2 = 1 without. Returns the scale code (0xFF
+// for a block holding a NaN or Inf, detected as in quantize_block).
 template <int RK>
 __device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1, float &m2) {
   uint32_t amax = 0;
@@ -199,8 +225,8 @@ __device__ __forceinline__ uint32_t block_scale(const float (&v)[32], float &m1,
     m1 = pow2_neg(e);
     m2 = 1.0f;
   } else {
-    m1 = e > 123 ? c : __fmul_rn(c, pow2_neg(min(e, 123)));
-    m2 = e > 123 ? pow2_neg(e) : 1.0f;
+    m1 = c;
+    m2 = pow2_neg(e);
   }
   return nonfinite ? 0xFFu : (uint32_t)(e + 127);
 }
@@ -270,6 +296,14 @@ __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_
 __device__ __forceinline__ int64_t code_offset(int64_t mn, int64_t kb, int64_t nslices) {
   return ((mn >> 4) * nslices + (kb >> 2)) * 1024 + (kb & 3) * 256 + (mn & 15) * 16;
 }
+// E4M3 codes (one byte per element): tile (g, q) is 2 KB at
+// (g * Kp/128 + q) * 2048; inside it the 16-element chunk j of row r is the
+// 16 bytes at j * 256 + r * 16. Block kb of row mn is chunks 2 (kb % 4) and
+// 2 (kb % 4) + 1; this returns the first one's address (the second is 256
+// bytes on).
+__device__ __forceinline__ int64_t code_offset_e4m3(int64_t mn, int64_t kb, int64_t nslices) {
+  return ((mn >> 4) * nslices + (kb >> 2)) * 2048 + (kb & 3) * 512 + (mn & 15) * 16;
+}
 __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t mnp) {
   return (((kb >> 2) * (mnp >> 8) + (mn >> 8)) * 16 + (mn & 15)) * 64 + (kb & 3) * 16 +
          ((mn >> 4) & 15);
@@ -284,7 +318,7 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 // row r's 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging
 // writes and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
 // ---------------------------------------------------------------------------
-template <int ROT, int RND>
+template <int ROT, int RND, int FMT>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
@@ -364,15 +398,22 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
     return pick_word(w, (uint32_t)(i & 3)) >> 8;
   };
-  uint32_t out[4];
-  uint32_t s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
+  constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
+  uint32_t out[kWords];
+  uint32_t s = quantize_block<RotKind<ROT>::value, RND, FMT>(y, out, u24_of);
   if (!valid) {                                         // padding: zero codes, scale code 0
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = 0u;
+    for (int j = 0; j < kWords; ++j) out[j] = 0u;
     s = 0u;
   }
-  *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
-      make_uint4(out[0], out[1], out[2], out[3]);
+  if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
+    uint8_t *tp = codes + tile * 2048 + cb * 512 + rr * 16;
+    *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
+    *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
+  } else {
+    *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+  }
   scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
 }
 
@@ -384,7 +425,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
 // operand rows of one tile, so each store instruction writes whole 256-byte
 // block rows of eight tiles.
 // ---------------------------------------------------------------------------
-template <int ROT, int RND>
+template <int ROT, int RND, int FMT>
 __global__ __launch_bounds__(256) void quant_axis0_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
@@ -401,8 +442,11 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
   const int64_t kb_begin = (int64_t)blockIdx.y * rb;
   const int64_t kb_end = min(nkb_pad, kb_begin + rb);
 
+  constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
   for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
-    uint32_t oa[4] = {0u, 0u, 0u, 0u}, ob[4] = {0u, 0u, 0u, 0u};
+    uint32_t oa[kWords], ob[kWords];
+#pragma unroll
+    for (int j = 0; j < kWords; ++j) oa[j] = ob[j] = 0u;
     uint32_t sa = 0u, sb = 0u;                     // padding: zero codes, scale code 0
     if (kb < nkb && has_a) {
       float ya[32], yb[32];
@@ -446,7 +490,7 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
         const U4 w = sr_words(L >> 2, seed_lo, seed_hi);
         return pick_word(w, (uint32_t)(L & 3)) >> 8;
       };
-      if (RND == MX_K_ROUND_SR) {
+      if constexpr (RND == MX_K_ROUND_SR && FMT == kFmtE2M1) {
         quantize_pair_sr<RotKind<ROT>::value>(ya, yb, oa, ob, sa, sb,
                                                (uint64_t)(row0 * cols + c0), cols, seed_lo,
                                                seed_hi);
@@ -456,14 +500,23 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
           sb = 0u;
         }
       } else {
-        sa = quantize_block<RotKind<ROT>::value, RND>(ya, oa, u24_a);
-        if (has_b) sb = quantize_block<RotKind<ROT>::value, RND>(yb, ob, u24_b);
+        sa = quantize_block<RotKind<ROT>::value, RND, FMT>(ya, oa, u24_a);
+        if (has_b) sb = quantize_block<RotKind<ROT>::value, RND, FMT>(yb, ob, u24_b);
       }
     }
-    *reinterpret_cast<uint4 *>(codes + code_offset(c0, kb, nslices)) =
-        make_uint4(oa[0], oa[1], oa[2], oa[3]);
-    *reinterpret_cast<uint4 *>(codes + code_offset(c0 + 1, kb, nslices)) =
-        make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    if constexpr (FMT == kFmtE4M3) {
+      uint8_t *pa = codes + code_offset_e4m3(c0, kb, nslices);
+      uint8_t *pb = codes + code_offset_e4m3(c0 + 1, kb, nslices);
+      *reinterpret_cast<uint4 *>(pa) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+      *reinterpret_cast<uint4 *>(pa + 256) = make_uint4(oa[4], oa[5], oa[6], oa[7]);
+      *reinterpret_cast<uint4 *>(pb) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+      *reinterpret_cast<uint4 *>(pb + 256) = make_uint4(ob[4], ob[5], ob[6], ob[7]);
+    } else {
+      *reinterpret_cast<uint4 *>(codes + code_offset(c0, kb, nslices)) =
+          make_uint4(oa[0], oa[1], oa[2], oa[3]);
+      *reinterpret_cast<uint4 *>(codes + code_offset(c0 + 1, kb, nslices)) =
+          make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    }
     scales[scale_offset(c0, kb, mnp)] = (uint8_t)sa;
     scales[scale_offset(c0 + 1, kb, mnp)] = (uint8_t)sb;
   }
@@ -534,7 +587,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
       if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), s1_lo, s1_hi);
       return pick_word(w, (uint32_t)(i & 3)) >> 8;
     };
-    s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
+    s = quantize_block<RotKind<ROT>::value, RND, kFmtE2M1>(y, out, u24_of);
     if ((kb << 5) >= cols || !rows_live) {                // padding of the operand
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = 0u;
@@ -562,7 +615,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
         const uint64_t L = (uint64_t)((R0 + i) * cols + c);
         return pick_word(sr_words(L >> 2, s0_lo, s0_hi), (uint32_t)(L & 3)) >> 8;
       };
-      s = quantize_block<RotKind<ROT>::value, RND>(y, out, u24_of);
+      s = quantize_block<RotKind<ROT>::value, RND, kFmtE2M1>(y, out, u24_of);
     } else {                                              // K padding of the operand
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = 0u;
@@ -586,13 +639,13 @@ hipError_t launch_dual(const DualArgs &a, hipStream_t stream) {
                 a.codes0, a.scales0, a.seed0_lo, a.seed0_hi, gx);
 }
 
-template <int ROT, int RND>
+template <int ROT, int RND, int FMT>
 hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
     const int64_t mnp = (a.rows + 255) & ~(int64_t)255;
     const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
     const int64_t blocks = (ntiles + 3) / 4;
-    return launch(quant_axis1_kernel<ROT, RND>, dim3((unsigned)blocks), dim3(256), 0, stream,
+    return launch(quant_axis1_kernel<ROT, RND, FMT>, dim3((unsigned)blocks), dim3(256), 0, stream,
                   a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi);
   }
   const int threads = 256;
@@ -602,7 +655,7 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   const int rb = a.rb > 0 ? a.rb : 4;
   const int64_t gy = (nkb_pad + rb - 1) / rb;
   const int pair_loads = (a.ld % 2 == 0) && (reinterpret_cast<uintptr_t>(a.x) % 4 == 0) ? 1 : 0;
-  return launch(quant_axis0_kernel<ROT, RND>, dim3((unsigned)gx, (unsigned)gy), dim3(threads), 0,
+  return launch(quant_axis0_kernel<ROT, RND, FMT>, dim3((unsigned)gx, (unsigned)gy), dim3(threads), 0,
                 stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi, rb,
                 pair_loads);
 }
@@ -624,15 +677,26 @@ hipError_t quantize_dual_launch(const DualArgs &a, hipStream_t stream) {
 }
 
 hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream) {
+  if (a.fmt == 1) {                       // E4M3 comparator: nearest rounding only
+    if (a.round != MX_K_ROUND_RNE) return hipErrorInvalidValue;
+    switch (a.rotate) {
+      case 0: return launch_quant<0, 0, kFmtE4M3>(a, stream);
+      case 1: return launch_quant<1, 0, kFmtE4M3>(a, stream);
+      case 2: return launch_quant<2, 0, kFmtE4M3>(a, stream);
+      case 3: return launch_quant<3, 0, kFmtE4M3>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (a.fmt != 0) return hipErrorInvalidValue;
   switch (a.rotate * 2 + a.round) {
-    case 0: return launch_quant<0, 0>(a, stream);
-    case 1: return launch_quant<0, 1>(a, stream);
-    case 2: return launch_quant<1, 0>(a, stream);
-    case 3: return launch_quant<1, 1>(a, stream);
-    case 4: return launch_quant<2, 0>(a, stream);
-    case 5: return launch_quant<2, 1>(a, stream);
-    case 6: return launch_quant<3, 0>(a, stream);
-    case 7: return launch_quant<3, 1>(a, stream);
+    case 0: return launch_quant<0, 0, kFmtE2M1>(a, stream);
+    case 1: return launch_quant<0, 1, kFmtE2M1>(a, stream);
+    case 2: return launch_quant<1, 0, kFmtE2M1>(a, stream);
+    case 3: return launch_quant<1, 1, kFmtE2M1>(a, stream);
+    case 4: return launch_quant<2, 0, kFmtE2M1>(a, stream);
+    case 5: return launch_quant<2, 1, kFmtE2M1>(a, stream);
+    case 6: return launch_quant<3, 0, kFmtE2M1>(a, stream);
+    case 7: return launch_quant<3, 1, kFmtE2M1>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

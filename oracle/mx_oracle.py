@@ -569,23 +569,24 @@ def tile_codes_fp8(codes: np.ndarray) -> np.ndarray:
 
     Zero-padded to [MNp, Kp] like the FP4 layout; tile (g, q) -- rows
     16g..16g+15, K elements 128q..128q+127 -- is the 2 KB at byte
-    (g * Kp/128 + q) * 2048, and inside it 32-element block c of row r is the
-    32 bytes at c * 512 + r * 32, element i of the block at byte i.
+    (g * Kp/128 + q) * 2048. Inside it, the 16-element chunk j (K elements
+    16j..16j+15 of the slice) of row r is the 16 bytes at j * 256 + r * 16,
+    element k of the slice at (k // 16) * 256 + r * 16 + k % 16.
     """
     codes = np.asarray(codes, dtype=np.uint8)
     mn, k = codes.shape
     mnp, kp = padded_extents(mn, k)
     full = np.zeros((mnp, kp), np.uint8)
     full[:mn, :k] = codes
-    t = full.reshape(mnp // TILE_ROWS, TILE_ROWS, kp // TILE_K, 4, 32)     # g r q c byte
-    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)   # g q c r byte
+    t = full.reshape(mnp // TILE_ROWS, TILE_ROWS, kp // TILE_K, 8, 16)     # g r q j byte
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(-1)   # g q j r byte
 
 
 def untile_codes_fp8(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
     """Inverse of tile_codes_fp8."""
     mnp, kp = padded_extents(mn, k)
-    t = np.asarray(buf, np.uint8)[: mnp * kp].reshape(mnp // TILE_ROWS, kp // TILE_K, 4,
-                                                      TILE_ROWS, 32)
+    t = np.asarray(buf, np.uint8)[: mnp * kp].reshape(mnp // TILE_ROWS, kp // TILE_K, 8,
+                                                      TILE_ROWS, 16)
     return t.transpose(0, 3, 1, 2, 4).reshape(mnp, kp)[:mn, :k]
 
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mx
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_symbols():
@@ -56,6 +56,47 @@ def test_quantize_sizes():
     assert ei.value.status == -4
 
 
+def test_quantize_fp8_sizes():
+    # one code byte per element, scales as for MXFP4
+    assert mx.quantize_fp8_sizes(8192, 4096, 1) == (8192 * 4096, 8192 * 4096 // 32)
+    assert mx.quantize_fp8_sizes(37, 160, 1) == (256 * 256, 256 * 256 // 32)
+    assert mx.quantize_fp8_sizes(160, 37, 0) == (256 * 256, 256 * 256 // 32)
+    assert mx.quantize_fp8_sizes(0, 64, 1) == (0, 0)
+    with pytest.raises(mx.MxError) as ei:
+        mx.quantize_fp8_sizes(64, 48, 1)
+    assert ei.value.status == -2
+
+
+def _q8(lib, x, rows, cols, ld, axis=1, block=32, rot=1, codes=4096, scales=4096):
+    desc = mx.QTensorDesc()
+    return lib.mx_quantize_fp8(x, rows, cols, ld, axis, block, rot, 0, codes, scales,
+                               ctypes.byref(desc), None)
+
+
+def test_quantize_fp8_rejects_before_launch():
+    lib = mx.load_library()
+    P = 4096
+    assert _q8(lib, P, 64, 64, 64, block=16) == -4
+    assert _q8(lib, P, 64, 64, 64, axis=2) == -4
+    assert _q8(lib, P, 64, 64, 64, rot=4) == -4
+    assert _q8(lib, P, 64, 48, 64) == -2
+    assert _q8(lib, P, 64, 64, 68) == -3
+    assert _q8(lib, P + 2, 64, 64, 64) == -3
+    assert _q8(lib, P, 64, 64, 64, codes=P + 8) == -3
+    # 1 GiB of E4M3 codes is reached at half the FP4 element count
+    assert _q8(lib, P, 1 << 16, 1 << 14, 1 << 14) == -6
+    assert _q(lib, P, 1 << 16, 1 << 14, 1 << 14, codes=None) == -1   # FP4: within the limit
+    assert _q8(lib, None, 64, 64, 64) == -1
+
+
+def test_quantize_fp8_empty_fills_descriptor():
+    lib = mx.load_library()
+    desc = mx.QTensorDesc()
+    assert lib.mx_quantize_fp8(None, 0, 64, 64, 1, 32, 3, 9, None, None, ctypes.byref(desc),
+                               None) == 0
+    assert (desc.format, desc.round, desc.rotate, desc.seed) == (1, 0, 3, 9)
+
+
 def _q(lib, x, rows, cols, ld, axis=1, block=32, rot=1, rnd=0, codes=16, scales=16):
     desc = mx.QTensorDesc()
     return lib.mx_quantize(x, rows, cols, ld, axis, block, rot, rnd, 0, codes, scales,
@@ -93,10 +134,11 @@ def test_quantize_empty_is_a_noop_and_fills_descriptor():
     assert (desc.rows, desc.cols, desc.axis, desc.rotate, desc.round, desc.seed) == (0, 64, 1, 2, 1, 77)
 
 
-def _desc(rows, cols, axis, rot=1, rnd=0, seed=0, codes=4096, scales=4096):
+def _desc(rows, cols, axis, rot=1, rnd=0, seed=0, codes=4096, scales=4096, fmt=0):
     d = mx.QTensorDesc()
     d.codes, d.scales = codes, scales
     d.rows, d.cols, d.axis, d.block, d.rotate, d.round, d.seed = rows, cols, axis, 32, rot, rnd, seed
+    d.format = fmt
     return d
 
 
@@ -166,6 +208,11 @@ def test_linear_rejects_before_launch():
     bad = _desc(64, 128, 1)
     bad.block = 16
     assert _lin(lib, 0, bad, W) == -4
+    assert _lin(lib, 0, _desc(64, 128, 1, fmt=2), _desc(96, 128, 1, fmt=2)) == -4  # bad format
+    assert _lin(lib, 0, _desc(64, 128, 1, fmt=1, rnd=1), _desc(96, 128, 1, fmt=1, rnd=1)) == -4
+    assert _lin(lib, 0, _desc(64, 128, 1, fmt=1), W) == -5                # E4M3 with E2M1
+    assert _lin(lib, 0, X, _desc(96, 128, 1, fmt=1)) == -5
+    assert _lin(lib, 0, _desc(64, 128, 1, fmt=1), _desc(96, 128, 1, fmt=1), C=None) == -1
     assert lib.mx_linear(0, None, ctypes.byref(W), 4096, 96, 0, None) == -1
 
 

@@ -658,8 +658,9 @@ def test_e4m3_tiled_layout_addresses_and_roundtrip():
         assert tb.size == mnp * kp
         for m in range(mn):
             for kk in range(0, k, 5):
-                g, r, q, c = m // 16, m % 16, kk // 128, (kk % 128) // 32
-                assert tb[(g * (kp // 128) + q) * 2048 + c * 512 + r * 32 + kk % 32] == codes[m, kk]
+                g, r, q = m // 16, m % 16, kk // 128
+                j, i = (kk % 128) // 16, kk % 16
+                assert tb[(g * (kp // 128) + q) * 2048 + j * 256 + r * 16 + i] == codes[m, kk]
         full = oracle.untile_codes_fp8(tb, mnp, kp)
         assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
         assert np.array_equal(oracle.untile_codes_fp8(tb, mn, k), codes)
