@@ -33,12 +33,13 @@ PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense MXFP8 MFMA (the E4M3 comparator)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
-GEMM_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm.hip"
-GEMM_E4M3_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_gemm_e4m3.hip"
+CSRC = "mxfp4_microscaled_precision_amd/csrc/"
+GEMM_SRC = (CSRC + "mx_gemm.hip", CSRC + "mx_gemm_common.h")
+GEMM_E4M3_SRC = (CSRC + "mx_gemm_e4m3.hip", CSRC + "mx_gemm_common.h")
 WORKLOADS_REF = None
 GEMM_TRAFFIC = "profiles/gemm_{}_traffic.md"
 GEMM_E4M3_TRAFFIC = "profiles/gemm_e4m3_{}_traffic.md"
-QUANT_SRC = "mxfp4_microscaled_precision_amd/csrc/mx_quant.hip"
+QUANT_SRC = (CSRC + "mx_quant.hip", CSRC + "mx_device.h")
 QUANT_TRAFFIC = "profiles/quant_{}_traffic.md"
 QUANT_E4M3_TRAFFIC = "profiles/quant_e4m3_{}_traffic.md"
 
@@ -257,13 +258,21 @@ def cpu_baseline(r, reps):
     }
 
 
-def recorded_traffic(kernel_src, summary):
-    """HBM bytes per GEMM launch from the committed counter summary, or None
-    when the kernel source has changed since the counters were taken."""
+def sources_digest(paths):
+    """sha256[:16] over the concatenated kernel sources (repo-relative)."""
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_src, summary):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources have changed since the counters were taken."""
     try:
-        with open(os.path.join(ROOT, kernel_src), "rb") as fh:
-            digest = hashlib.sha256(fh.read()).hexdigest()[:16]
+        digest = sources_digest(kernel_src)
         with open(os.path.join(ROOT, summary)) as fh:
             fields = dict(ln.strip()[2:].split(": ", 1) for ln in fh
                           if ln.startswith("- ") and ": " in ln)
