@@ -1,6 +1,5 @@
 // Device helpers shared by the gfx950 kernels: Philox4x32-10, bf16 widening,
-// the E8M0 block exponent, the E2M1 element encoders and the E4M3 encoder of
-// the MXFP8 comparator.
+// the E8M0 block exponent and the E2M1 element encoders.
 //
 // The MXFP4 format (36Kr article "Neue Studie von AMD durchbricht die
 // bestehende Erkenntnis ...", section "Was ist MXFP4?"): 32-element blocks,
@@ -131,24 +130,6 @@ __device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
   const float thr = __fmul_rn(__fsub_rn(bits_f(ab), lo), inv_gap24);
   const uint32_t up = (float)u24 < thr ? 1u : 0u;
   return idx >= 7 ? 7u : idx + up;                // a >= 6 saturates (not randomised)
-}
-
-// ---------------------------------------------------------------------------
-// E4M3 element of the MXFP8 comparator (OCP: bias 7, subnormal step 2^-9,
-// largest finite 448, no Inf). Code of t with |t| < 512 -- the block scaling
-// keeps every element there -- rounded to nearest even and saturated at 448
-// (magnitude code 0x7E); the sign bit is t's.
-//  * |t| >= 2^-6 (normal): rounding the fp32 mantissa to 3 bits is an integer
-//    add on the bit pattern (carries move into the exponent), and the code is
-//    the top bits minus the exponent-bias difference (127 - 7) << 3.
-//  * |t| < 2^-6: the code is the number of 2^-9 steps, rint(|t| * 512) (an
-//    exact scaling; v_rndne rounds ties to even). 8 steps are 2^-6, code 8.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_rne(float t) {
-  const uint32_t b = f_bits(t), ab = b & 0x7FFFFFFFu;
-  const uint32_t sub = (uint32_t)__builtin_rintf(bits_f(ab) * 512.0f);
-  const uint32_t nrm = min((ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20, 1086u) - 960u;
-  return (ab < 0x3C800000u ? sub : nrm) | ((b >> 24) & 0x80u);
 }
 
 }  // namespace mx

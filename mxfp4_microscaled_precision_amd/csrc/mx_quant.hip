@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -65,6 +67,13 @@ __device__ __forceinline__ void butterfly16x2(float (&y)[32]) {
       }
     }
   }
+}
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+
+// |t| clamped to 448, E4M3's largest finite value (one v_med3_f32).
+__device__ __forceinline__ float sat448(float t) {
+  return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
 }
 
 // Element formats: the E2M1 elements of MXFP4, and the E4M3 elements of the
@@ -118,7 +127,8 @@ __device__ __forceinline__ float rot_norm() {
 //    even and saturates at +-6 exactly like the threshold rule (checked over
 //    every fp32 pattern); two elements per instruction, element 2j in the low
 //    nibble. SR: integer rule of e2m1_sr_mag with the Philox uniform. E4M3
-//    (nearest only): e4m3_rne, one code byte per element.
+//    (nearest only): the hardware fp8 convert behind a clamp to +-448, one
+//    code byte per element.
 template <int RK, int RND, int FMT, typename U24Fn>
 __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32],
                                                    uint32_t (&out)[FMT == kFmtE4M3 ? 8 : 4],
@@ -169,10 +179,20 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32],
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], m1), m2);
   }
   if constexpr (FMT == kFmtE4M3) {
+    // v_cvt_scalef32_pk_fp8_f32 at scale 1.0 rounds to the nearest E4M3
+    // value, ties to even, exactly like the integer rule below 464 (checked
+    // over every fp32 value of magnitude below 512) but turns larger
+    // magnitudes into NaN; the med3 clamp to +-448 makes it saturate.
+    // Element 4j + i goes to byte i of word j.
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      out[j] = e4m3_rne(t[4 * j]) | (e4m3_rne(t[4 * j + 1]) << 8) |
-               (e4m3_rne(t[4 * j + 2]) << 16) | (e4m3_rne(t[4 * j + 3]) << 24);
+    for (int j = 0; j < 8; ++j) {
+      v2i16 w = {0, 0};
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, sat448(t[4 * j]), sat448(t[4 * j + 1]),
+                                                   1.0f, false);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, sat448(t[4 * j + 2]),
+                                                   sat448(t[4 * j + 3]), 1.0f, true);
+      out[j] = (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
+    }
   } else if (RND == MX_K_ROUND_SR) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = 0u;
@@ -310,14 +330,18 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// axis = 1 (blocks run along a source row): one wave per output tile (16 rows
-// x 128 K elements). The tile's 4 KB of bf16 is read with each load
-// instruction covering four whole 256-byte row pieces, staged in LDS, and
-// lane l then takes row (l & 15), block (l >> 4): 64 bytes in, 16 code bytes
-// out at tile + 16 l (the wave writes its 1 KB tile in one go). LDS holds
-// row r's 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging
-// writes and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
+// axis = 1 (blocks run along a source row): a wave encodes one output tile
+// (16 rows x 128 K elements) at a time and walks the tiles wave_id,
+// wave_id + waves, ...; the next tile's loads are in flight while the current
+// one is encoded. The tile's 4 KB of bf16 is read with each load instruction
+// covering four whole 256-byte row pieces, staged in LDS, and lane l then
+// takes row (l & 15), block (l >> 4): 64 bytes in, 16 code bytes out at
+// tile + 16 l (the wave writes its 1 KB tile in one go). LDS holds row r's
+// 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging writes
+// and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
 // ---------------------------------------------------------------------------
+constexpr int kAxis1WgPerCu = 4;   // 16 waves per compute unit (measured best of 2, 4, 8)
+
 template <int ROT, int RND, int FMT>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -329,92 +353,100 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
   const int64_t nslices = (cols + 127) >> 7;
   const int64_t ntiles = (mnp >> 4) * nslices;
   const int wv = threadIdx.x >> 6;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t tile = (int64_t)blockIdx.x * 4 + wv;
   if (tile >= ntiles) return;
   const int lane = threadIdx.x & 63;
-  const int64_t g = tile / nslices;
-  const int64_t q = tile - g * nslices;
   uint8_t *st = stage[wv];
-
-  // staging: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
-  {
-    const int ch = lane & 15;
-    const int64_t k = q * 128 + ch * 8;                 // first element of the chunk
-    u32x4 v[4];
+  const int ch = lane & 15;
+  // staging loads of a tile: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
+  u32x4 v[4];
+  auto load_tile = [&](int64_t t) {
+    const int64_t tg = t / nslices;
+    const int64_t k = (t - tg * nslices) * 128 + ch * 8;   // first element of the chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
-      const int64_t r = g * 16 + rr;
+      const int64_t r = tg * 16 + rr;
       v[j] = (r < rows && k < cols)
                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + r * ld + k))
                  : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  load_tile(tile);
+  for (; tile < ntiles; tile += stride) {
+    const int64_t g = tile / nslices;
+    const int64_t q = tile - g * nslices;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
       *reinterpret_cast<u32x4 *>(st + rr * 256 + ((ch ^ rr) << 4)) = v[j];
     }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  const int rr = lane & 15, cb = lane >> 4;
-  const int64_t r = g * 16 + rr;
-  const int64_t kb = q * 4 + cb;
-  const bool valid = r < rows && (kb << 5) < cols;
-  float y[32];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((cb * 4 + j) ^ rr) << 4));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      y[8 * j + 2 * t] = bits_f(d[t] << 16);
-      y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
-    }
-  }
-  if (ROT == MX_K_ROT_RAND_SIGN) {
-    // the tile's 128 reduction indices need 32 Philox calls: lanes 0..31
-    // make one each, the sign bits meet in LDS as one nibble per call
-    uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
-    if (lane < 32) {
-      const U4 sw = sign_words((uint32_t)(q * 32 + lane), seed_lo);
-      sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
-    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint32_t mask = 0u;
+    if (tile + stride < ntiles) load_tile(tile + stride);   // next tile's loads in flight
+
+    const int rr = lane & 15, cb = lane >> 4;
+    const int64_t r = g * 16 + rr;
+    const int64_t kb = q * 4 + cb;
+    const bool valid = r < rows && (kb << 5) < cols;
+    float y[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mask |= sg[cb * 8 + j] << (4 * j);
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((cb * 4 + j) ^ rr) << 4));
 #pragma unroll
-    for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
-  }
-  rotate_block<ROT>(y);
-  // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
-  const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
-  U4 w{0u, 0u, 0u, 0u};
-  auto u24_of = [&](int i) -> uint32_t {
-    if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
-    return pick_word(w, (uint32_t)(i & 3)) >> 8;
-  };
-  constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
-  uint32_t out[kWords];
-  uint32_t s = quantize_block<RotKind<ROT>::value, RND, FMT>(y, out, u24_of);
-  if (!valid) {                                         // padding: zero codes, scale code 0
+      for (int t = 0; t < 4; ++t) {
+        y[8 * j + 2 * t] = bits_f(d[t] << 16);
+        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+      }
+    }
+    if (ROT == MX_K_ROT_RAND_SIGN) {
+      // the tile's 128 reduction indices need 32 Philox calls: lanes 0..31
+      // make one each, the sign bits meet in LDS as one nibble per call
+      uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
+      if (lane < 32) {
+        const U4 sw = sign_words((uint32_t)(q * 32 + lane), seed_lo);
+        sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint32_t mask = 0u;
 #pragma unroll
-    for (int j = 0; j < kWords; ++j) out[j] = 0u;
-    s = 0u;
+      for (int j = 0; j < 8; ++j) mask |= sg[cb * 8 + j] << (4 * j);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
+    }
+    rotate_block<ROT>(y);
+    // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
+    const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
+    U4 w{0u, 0u, 0u, 0u};
+    auto u24_of = [&](int i) -> uint32_t {
+      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
+      return pick_word(w, (uint32_t)(i & 3)) >> 8;
+    };
+    constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
+    uint32_t out[kWords];
+    uint32_t s = quantize_block<RotKind<ROT>::value, RND, FMT>(y, out, u24_of);
+    if (!valid) {                                         // padding: zero codes, scale code 0
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) out[j] = 0u;
+      s = 0u;
+    }
+    if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
+      uint8_t *tp = codes + tile * 2048 + cb * 512 + rr * 16;
+      *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
+      *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
+    } else {
+      *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
+          make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
+    __builtin_amdgcn_wave_barrier();        // all lanes done with st before it is rewritten
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
-    uint8_t *tp = codes + tile * 2048 + cb * 512 + rr * 16;
-    *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
-    *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
-  } else {
-    *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
-        make_uint4(out[0], out[1], out[2], out[3]);
-  }
-  scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
 }
 
 // ---------------------------------------------------------------------------
@@ -644,7 +676,7 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
     const int64_t mnp = (a.rows + 255) & ~(int64_t)255;
     const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
-    const int64_t blocks = (ntiles + 3) / 4;
+    const int64_t blocks = std::min<int64_t>((ntiles + 3) / 4, (int64_t)cu_count() * kAxis1WgPerCu);
     return launch(quant_axis1_kernel<ROT, RND, FMT>, dim3((unsigned)blocks), dim3(256), 0, stream,
                   a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi);
   }
