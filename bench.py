@@ -47,8 +47,10 @@ QUANT_E4M3_TRAFFIC = "profiles/quant_e4m3_{}_traffic.md"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # about 40 ms of back-to-back steps: the clock settles under sustained load
+    # (measured: 10 warmup steps time the step ~15% slow, 400 and more agree)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="fprop_q_proj")
     ap.add_argument("--variant", default=None)
     ap.add_argument("--format", default="fp4_e2m1", choices=("fp4_e2m1", "fp8_e4m3"),
@@ -163,12 +165,36 @@ class Runner:
         return (self.M + self.N) * self.K * (self.code_bytes() + 1.0 / 32) + self.M * self.N * ob
 
 
-def time_loop(fn, iters, warmup):
+SETTLE_MS = 40.0   # sustained load before timing: the clock settles in about this long
+
+
+def settle(fn, min_ms=SETTLE_MS):
+    """Run fn(i) back to back for at least min_ms of GPU time (untimed
+    warmup sized from a short first burst); returns the number of calls."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(5):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1) / 5, 1e-3)
+    n = int(math.ceil(min_ms / per))
+    for i in range(n):
+        fn(5 + i)
+    torch.cuda.synchronize()
+    return 5 + n
+
+
+def time_loop(fn, iters, warmup=None):
     """Average ms per call of fn(i) over `iters` back-to-back calls, between
     one pair of HIP events on the current stream (the stream the library
     launches on)."""
     import torch
-    for i in range(warmup):
+    if warmup is None:
+        settle(fn)
+    for i in range(warmup or 0):
         fn(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -181,12 +207,15 @@ def time_loop(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters
 
 
-def measure(r, steps, warmup):
+def measure(r, steps, warmup=None):
     """The timed region: `steps` whole steps (quantize A, quantize B, GEMM)
-    back to back. Then each kernel alone, back to back, for its average
+    back to back, after `warmup` untimed steps (None: as many as SETTLE_MS of
+    load takes). Then each kernel alone, back to back, for its average
     launch duration (events between the kernels of a step would add gaps)."""
     import torch
-    for i in range(warmup):
+    if warmup is None:
+        settle(r.step)
+    for i in range(warmup or 0):
         r.step(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -356,7 +385,7 @@ def main():
         "gemm_only_tflops": round(res["gemm_tflops"], 2),
     }
     if not fp8 and r.rnd == "rne":
-        out["fp8_comparator"] = fp8_comparator(mx, w, variant, max(10, args.steps // 2), res)
+        out["fp8_comparator"] = fp8_comparator(mx, w, variant, max(10, args.steps // 4), res)
         print(f"[bench] fp8 comparator {out['fp8_comparator']}", file=sys.stderr, flush=True)
     if args.all:
         extra = {}
@@ -368,7 +397,7 @@ def main():
                 if name == w.name and v[0] == variant:
                     continue
                 rr = Runner(mx, wl, v[0], tensors=t)
-                m = measure(rr, max(10, args.steps // 2), 3)
+                m = measure(rr, max(10, args.steps // 4))
                 extra[f"{name}/{v[0]}"] = {k: round(val, 3) for k, val in m.items()}
                 print(f"[bench] {name}/{v[0]}: {m['tflops']:.1f} TFLOP/s", file=sys.stderr,
                       flush=True)
@@ -380,7 +409,7 @@ def main():
         out["wgrad_gate_proj_quant_error"] = output_mse(mx, wg, [v[0] for v in wg.variants])
         print(f"[bench] quant error {out['wgrad_gate_proj_quant_error']}", file=sys.stderr,
               flush=True)
-        out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 5))
+        out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 20))
     if args.structural or args.all:
         out["structural_error"] = structural_error(mx)
         print("[bench] structural error done", file=sys.stderr, flush=True)
@@ -405,7 +434,7 @@ def fp8_comparator(mx, w, variant, steps, fp4_res):
     theory twice FP8's compute; the MXFP4 training step ran about 20% faster
     than the FP8 baseline)."""
     r8 = Runner(mx, w, variant, fmt="fp8_e4m3")
-    m8 = measure(r8, steps, 3)
+    m8 = measure(r8, steps)
     fl = r8.flops()
     out = {
         "ms_per_step": round(m8["ms_per_step"], 5),
@@ -490,9 +519,9 @@ def dual_quant_bench(mx, steps):
                     raise RuntimeError("mx_quantize failed")
             return f
 
-        t_d = time_loop(dual, steps, 3) * 1e3
-        t_1 = time_loop(single(1), steps, 3) * 1e3
-        t_0 = time_loop(single(0), steps, 3) * 1e3
+        t_d = time_loop(dual, steps) * 1e3
+        t_1 = time_loop(single(1), steps) * 1e3
+        t_0 = time_loop(single(0), steps) * 1e3
         n = rows * cols
         res[f"{wname}/{tname} {rows}x{cols}"] = {
             "dual_us": round(t_d, 2), "axis1_us": round(t_1, 2), "axis0_us": round(t_0, 2),
@@ -581,7 +610,7 @@ def bench_block(mx, wls, steps):
             cache[key] = workload_tensors(wl)
         for v in wl.variants:
             rr = Runner(mx, wl, v[0], tensors=cache[key], min_bytes=0)
-            m = measure(rr, steps, 2)
+            m = measure(rr, steps)
             d = res.setdefault(v[0], {"flops": 0.0, "ms": 0.0, "saved_ms": 0.0, "ops": {}})
             d["flops"] += rr.flops()
             d["ms"] += m["ms_per_step"]
