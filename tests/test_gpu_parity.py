@@ -351,3 +351,18 @@ def test_structural_error_harness_separates_fixed_and_changing_errors(mx):
         assert abs(v[det]["mean_rel_err"]["16"] - s[0]) <= 1e-6 * s[0], det
     for rnd in ("rand_sign_hadamard", "no_rotation_sr", "hadamard_sr"):
         assert v[rnd]["mean_rel_err"]["16"] < 0.7 * v[rnd]["single_step_rel_err"][0], rnd
+
+
+def test_quantize_axis1_many_tiles_ragged(mx):
+    """More tiles than resident waves (8200 x 2048: 8448 tiles of 16 x 128, the
+    last 256-row panel ragged), so waves walk several tiles; every byte is
+    checked, padding included, in both element formats."""
+    rng = np.random.default_rng(61)
+    x = _rand_bits(rng, (8200, 2048), 2.0)
+    q = mx.quantize(to_dev(x), axis=1, rotate="hadamard", round="rne")
+    q8 = mx.quantize_fp8(to_dev(x), axis=1, rotate="hadamard")
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, 1, rotate="hadamard"), "fp4")
+    ref8 = oracle.quantize_ref(x, 1, rotate="hadamard", fmt="fp8_e4m3")
+    assert np.array_equal(host_u8(q8.codes), oracle.tile_codes_fp8(ref8.codes))
+    assert np.array_equal(host_u8(q8.scales), oracle.tile_scales(ref8.scales, 2048))
