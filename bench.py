@@ -315,8 +315,8 @@ def recorded_traffic(kernel_src, summary):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(sharding is described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
         sys.exit(2)
     import torch
 

@@ -44,7 +44,7 @@ typedef enum mx_status {
   MX_ERR_ALIGN = -3,       /* a device pointer or leading dimension is misaligned */
   MX_ERR_ARG = -4,         /* bad enum value, block != 32, axis wrong for the op  */
   MX_ERR_MISMATCH = -5,    /* A and B quantized with different rotations / sign seeds / formats */
-  MX_ERR_UNSUPPORTED = -6, /* valid request this build does not implement        */
+  MX_ERR_UNSUPPORTED = -6, /* valid request the library does not implement       */
   MX_ERR_HIP = -7          /* the HIP runtime reported a launch error            */
 } mx_status;
 
