@@ -366,3 +366,20 @@ def test_quantize_axis1_many_tiles_ragged(mx):
     ref8 = oracle.quantize_ref(x, 1, rotate="hadamard", fmt="fp8_e4m3")
     assert np.array_equal(host_u8(q8.codes), oracle.tile_codes_fp8(ref8.codes))
     assert np.array_equal(host_u8(q8.scales), oracle.tile_scales(ref8.scales, 2048))
+
+
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("shape,ld", [((160, 100), 100), ((256, 64), 64), ((96, 516), 520),
+                                      ((32, 4), 8)])
+def test_quantize_axis0_sr_quad_shared_philox(mx, rot, shape, ld):
+    """Axis-0 stochastic rounding with cols % 4 == 0, where the four lanes of a
+    quad share each Philox call: ragged and aligned column counts, padded
+    rows, a row stride above cols; bit-exact against the oracle."""
+    rng = np.random.default_rng(71 + shape[1])
+    x = _rand_bits(rng, shape, 1.5)
+    t = to_dev(x) if ld == shape[1] else to_dev_strided(x, ld=ld)
+    seed = 0xBEEF | (1 << 32)
+    q = mx.quantize(t, axis=0, rotate=rot, round="sr", seed=seed)
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, 0, rotate=rot, rounding="sr", seed=seed),
+             f"rot={rot} shape={shape} ld={ld}")
