@@ -776,7 +776,9 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   const int threads = 256;
   const int64_t mnp = (a.cols + 255) & ~(int64_t)255;
   const int64_t nkb_pad = ((a.rows + 127) >> 7) * 4;
-  const int rb = a.rb > 0 ? a.rb : 4;
+  // 32-row blocks per lane: measured best 1 for nearest rounding (7-16% faster
+  // than 4), 2 for stochastic rounding
+  const int rb = a.rb > 0 ? a.rb : (RND == MX_K_ROUND_SR ? 2 : 1);
   const int64_t gy = (nkb_pad + rb - 1) / rb;
   // one column per lane, quads sharing Philox: measured 15-18% faster with a
   // rotation, 2-11% slower without one (there the column-pair kernel stays)
