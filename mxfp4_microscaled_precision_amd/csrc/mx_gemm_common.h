@@ -20,10 +20,22 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 
+// Two fp32 values as packed bf16, the first in the low half: gfx950's
+// v_cvt_pk_bf16_f32, round to nearest even. Measured on every one of the
+// 2^32 fp32 patterns: identical to the integer rule (u + 0x7FFF + bit 16)
+// >> 16 for non-NaN u, and to (u >> 16) | 0x40 (sign and payload kept,
+// quieted) for NaN. One instruction per two elements instead of about six
+// per element, which kept the epilogue's VALU work off the matrix core's
+// critical path.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  return (uint16_t)pack_bf16x2_rne(f, 0.f);
 }
 
 // Generic epilogue store of one quad: lane (lr, lg) of a 16x16 tile holds
@@ -98,8 +110,8 @@ __device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc
   if (vec_ok && col + 3 < g.N) {
     if (OUT_BF16) {
       uint2 v;
-      v.x = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-      v.y = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+      v.x = pack_bf16x2_rne(acc[0], acc[1]);
+      v.y = pack_bf16x2_rne(acc[2], acc[3]);
       *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col) = v;
     } else {
       *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col) =
