@@ -79,6 +79,8 @@ constexpr int kStageSB = kBN * 4;
 constexpr int kStageBytes = kStageA + kStageB + kStageSA + kStageSB;
 constexpr int kRing = 4;                           // stage buffers (136 KB)
 constexpr int kAhead = kRing - 1;                  // stages in flight
+constexpr int kSlab = 2048;                        // epilogue staging per consumer wave
+static_assert(kRing * kStageBytes + kConsumers * kSlab <= 160 * 1024, "LDS");
 
 // Row I of a consumer's stage: read A fragment I + 2 (and, in row S - 1, every
 // A fragment still unread), then the 4 MFMAs of row I. Rows from S on read
@@ -111,6 +113,67 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v
   (consume_row<LO + I, S>(acc, bf, af, a_base, sb, sa), ...);
 }
 
+// Stores a finished 128x64 wave tile (rows row0.., columns col0..) through
+// the wave's private 2 KB LDS slab, 16 rows at a time: lane (lr, lg) writes
+// its quads of row lr, then lane l reads back 16 contiguous bytes of row
+// l / 8 (chunk l % 8) and stores them, so that each store instruction
+// writes eight whole 128-byte row segments instead of sixteen 32-byte
+// pieces. Chunk c of slab row r sits at chunk c ^ (r & 7) (fewer bank
+// conflicts for the column-strided writes). A wave's LDS operations run in
+// order, so a slab row group is read back before the next overwrites it.
+// Measured against the direct quad stores (bitwise identical output): Fprop
+// 70.7 -> 61.0 us, Dgrad 236 -> 204 us, Wgrad (fp32 out) 228 -> 222 us.
+// Wave tiles that cross the edge of C, or a C that is not 16-byte aligned,
+// keep the quad stores.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&acc)[8][4],
+                                               uint8_t *slab, int64_t row0, int64_t col0, int lr,
+                                               int lg) {
+  // Opaque copies: keeps the compiler from hoisting these lane addresses
+  // out of the stage loop, where they would hold registers the MFMA loop
+  // needs.
+  asm volatile("" : "+v"(lr), "+v"(lg));
+  const int lane = lg * 16 + lr;
+  const int rr = lane >> 3, ch = lane & 7;                 // read-back row (of 8), chunk
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int h = 0; h < (OUT_BF16 ? 1 : 2); ++h) {
+      if (OUT_BF16) {
+        // row of 64 bf16 = 128 B: quad j of lane lg is bytes 32 j + 8 lg
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 2 * j + (lg >> 1);
+          uint2 v;
+          v.x = pack_bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+          v.y = pack_bf16x2_rne(acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<uint2 *>(slab + lr * 128 + ((c ^ (lr & 7)) << 4) + ((lg & 1) << 3)) = v;
+        }
+      } else {
+        // columns 32 h .. 32 h + 31 as fp32 = 128 B: quad 2 h + jj of lane
+        // lg is bytes 64 jj + 16 lg
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int c = jj * 4 + lg;
+          *reinterpret_cast<v4f *>(slab + lr * 128 + ((c ^ (lr & 7)) << 4)) = acc[i][2 * h + jj];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = k * 8 + rr;
+        const uint4 d = *reinterpret_cast<const uint4 *>(slab + r * 128 + ((ch ^ (r & 7)) << 4));
+        const int64_t row = row0 + i * 16 + r;
+        if (OUT_BF16)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col0 +
+                                     ch * 8) = d;
+        else
+          *reinterpret_cast<uint4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col0 +
+                                     h * 32 + ch * 4) = d;
+      }
+    }
+  }
+}
+
 // The consumers' stage loop. The consumers of wave row 0 wait at the barrier
 // that publishes stage G, then read its first fragments. Those of wave row 1
 // (SHIFTED; waves 4..7, so each SIMD holds one of each kind) run most of a
@@ -128,9 +191,10 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v
 template <int OUT_BF16, bool SHIFTED>
 __device__ __forceinline__ void consumer_loop(const GemmArgs &g, const uint8_t *smem, int total,
                                               int nslices, int bid, int grid, int tm, int tn,
-                                              bool vec_ok, uint32_t a_off, uint32_t b_off,
-                                              uint32_t sa_off, uint32_t sb_off, int lr, int lg,
-                                              int wm, int wn) {
+                                              bool vec_ok, bool line_ok, uint32_t a_off,
+                                              uint32_t b_off, uint32_t sa_off, uint32_t sb_off,
+                                              int lr, int lg, int wm, int wn) {
+  uint8_t *slab = const_cast<uint8_t *>(smem) + kRing * kStageBytes + (wm * 4 + wn) * kSlab;
   constexpr int kSplit = 6;
   v4f acc[8][4];
 #pragma unroll
@@ -165,15 +229,21 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, const uint8_t *
       int mi, ni;
       tile_coords(bid + ck * grid, tm, tn, &mi, &ni);
       ++ck;
-      const int64_t row0 = (int64_t)mi * kBM + wm * 128 + lr;
-      const int64_t col0 = (int64_t)ni * kBN + wn * 64 + 4 * lg;
+      const int64_t rbase = (int64_t)mi * kBM + wm * 128, cbase = (int64_t)ni * kBN + wn * 64;
+      if (line_ok && rbase + 128 <= g.M && cbase + 64 <= g.N) {
+        store_tile_lds<OUT_BF16>(g, acc, slab, rbase, cbase, lr, lg);
+      } else {
+        const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
-          acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
   if (!SHIFTED) __syncthreads();                           // the shifted consumers' last barrier
@@ -185,7 +255,7 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, const uint8_t *
 // tile's first stages are already in flight.
 template <int OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes + kConsumers * kSlab];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -270,6 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   }
 
   // consumers
+  // whole 16-byte stores: C and its row pitch 16-byte aligned
+  const bool line_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
+                       ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) &&
                       ((g.ldc & 3) == 0);
   const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
@@ -281,11 +354,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + s_slot + wm * 8;
   const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + s_slot + wn * 4;
   if (wm == 1)
-    consumer_loop<OUT_BF16, true>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, a_off,
-                                  b_off, sa_off, sb_off, lr, lg, wm, wn);
+    consumer_loop<OUT_BF16, true>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, line_ok,
+                                  a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
   else
-    consumer_loop<OUT_BF16, false>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, a_off,
-                                   b_off, sa_off, sb_off, lr, lg, wm, wn);
+    consumer_loop<OUT_BF16, false>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, line_ok,
+                                   a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
 }
 
 template <int OUT_BF16>
