@@ -122,5 +122,68 @@ __device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc
   }
 }
 
+constexpr int kSlab = 2048;                        // epilogue staging per 128x64 wave tile
+
+// Stores a finished 128x64 wave tile (rows row0.., columns col0..) through
+// the wave's private 2 KB LDS slab, 16 rows at a time: lane (lr, lg) writes
+// its quads of row lr, then lane l reads back 16 contiguous bytes of row
+// l / 8 (chunk l % 8) and stores them, so that each store instruction
+// writes eight whole 128-byte row segments instead of sixteen 32-byte
+// pieces. Chunk c of slab row r sits at chunk c ^ (r & 7) (fewer bank
+// conflicts for the column-strided writes). A wave's LDS operations run in
+// order, so a slab row group is read back before the next overwrites it.
+// Measured on the MXFP4 kernel against the direct quad stores (bitwise
+// identical output): Fprop 70.7 -> 61.0 us, Dgrad 236 -> 204 us, Wgrad (fp32
+// out) 228 -> 222 us. Wave tiles that cross the edge of C, or a C that is not
+// 16-byte aligned, keep the quad stores.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&acc)[8][4],
+                                               uint8_t *slab, int64_t row0, int64_t col0, int lr,
+                                               int lg) {
+  // Opaque copies: keeps the compiler from hoisting these lane addresses
+  // out of the stage loop, where they would hold registers the MFMA loop
+  // needs.
+  asm volatile("" : "+v"(lr), "+v"(lg));
+  const int lane = lg * 16 + lr;
+  const int rr = lane >> 3, ch = lane & 7;                 // read-back row (of 8), chunk
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int h = 0; h < (OUT_BF16 ? 1 : 2); ++h) {
+      if (OUT_BF16) {
+        // row of 64 bf16 = 128 B: quad j of lane lg is bytes 32 j + 8 lg
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 2 * j + (lg >> 1);
+          uint2 v;
+          v.x = pack_bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+          v.y = pack_bf16x2_rne(acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<uint2 *>(slab + lr * 128 + ((c ^ (lr & 7)) << 4) + ((lg & 1) << 3)) = v;
+        }
+      } else {
+        // columns 32 h .. 32 h + 31 as fp32 = 128 B: quad 2 h + jj of lane
+        // lg is bytes 64 jj + 16 lg
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int c = jj * 4 + lg;
+          *reinterpret_cast<v4f *>(slab + lr * 128 + ((c ^ (lr & 7)) << 4)) = acc[i][2 * h + jj];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = k * 8 + rr;
+        const uint4 d = *reinterpret_cast<const uint4 *>(slab + r * 128 + ((ch ^ (r & 7)) << 4));
+        const int64_t row = row0 + i * 16 + r;
+        if (OUT_BF16)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col0 +
+                                     ch * 8) = d;
+        else
+          *reinterpret_cast<uint4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col0 +
+                                     h * 32 + ch * 4) = d;
+      }
+    }
+  }
+}
+
 }  // namespace gemm
 }  // namespace mx

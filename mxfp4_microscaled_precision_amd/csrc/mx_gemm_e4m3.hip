@@ -104,7 +104,7 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v
 // overlaps the previous tile's last stage.
 template <int OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes + 8 * kSlab];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,6 +167,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
   // ---- consumers
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) &&
                       ((g.ldc & 3) == 0);
+  // whole 16-byte stores through the wave's LDS slab: C and its row pitch
+  // 16-byte aligned
+  const bool line_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
+                       ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
+  uint8_t *slab = smem + kRing * kStageBytes + wave * kSlab;
   const uint32_t a_off = (uint32_t)((wm * 8) * 2048 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 2048 + lane * 16);
   const uint32_t s_slot = (uint32_t)((lr * 4 + lg) * 16);
@@ -200,15 +205,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
       int mi, ni;
       tile_coords(bid + ck * grid, tm, tn, &mi, &ni);
       ++ck;
-      const int64_t row0 = (int64_t)mi * kBM + wm * 128 + lr;
-      const int64_t col0 = (int64_t)ni * kBN + wn * 64 + 4 * lg;
+      const int64_t rbase = (int64_t)mi * kBM + wm * 128, cbase = (int64_t)ni * kBN + wn * 64;
+      if (line_ok && rbase + 128 <= g.M && cbase + 64 <= g.N) {
+        store_tile_lds<OUT_BF16>(g, acc, slab, rbase, cbase, lr, lg);
+      } else {
+        const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
-          acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
