@@ -350,33 +350,45 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][4096];
   __shared__ __attribute__((aligned(16))) uint8_t signs_lds[ROT == MX_K_ROT_RAND_SIGN ? 4 : 1][128];
   const int64_t mnp = (rows + 255) & ~(int64_t)255;
-  const int64_t nslices = (cols + 127) >> 7;
-  const int64_t ntiles = (mnp >> 4) * nslices;
+  // Tile counts fit 32 bits: the host refuses operands of 1 GiB of codes.
+  const uint32_t nslices = (uint32_t)((cols + 127) >> 7);
+  const uint32_t ntiles = (uint32_t)(mnp >> 4) * nslices;
   const int wv = threadIdx.x >> 6;
-  const int64_t stride = (int64_t)gridDim.x * 4;
-  int64_t tile = (int64_t)blockIdx.x * 4 + wv;
+  const uint32_t stride = gridDim.x * 4u;
+  uint32_t tile = blockIdx.x * 4u + (uint32_t)wv;
   if (tile >= ntiles) return;
   const int lane = threadIdx.x & 63;
   uint8_t *st = stage[wv];
   const int ch = lane & 15;
+  // (row group, K slice) of this tile and of the next one; the stride's own
+  // split advances them without a division per tile
+  const uint32_t st_g = stride / nslices, st_q = stride - st_g * nslices;
+  uint32_t g = tile / nslices, q = tile - g * nslices;
+  auto advance = [&](uint32_t &tg, uint32_t &tq) {
+    tq += st_q;
+    tg += st_g;
+    if (tq >= nslices) {
+      tq -= nslices;
+      ++tg;
+    }
+  };
   // staging loads of a tile: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
   u32x4 v[4];
-  auto load_tile = [&](int64_t t) {
-    const int64_t tg = t / nslices;
-    const int64_t k = (t - tg * nslices) * 128 + ch * 8;   // first element of the chunk
+  auto load_tile = [&](uint32_t tg, uint32_t tq) {
+    const int64_t k = (int64_t)tq * 128 + ch * 8;           // first element of the chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
-      const int64_t r = tg * 16 + rr;
+      const int64_t r = (int64_t)tg * 16 + rr;
       v[j] = (r < rows && k < cols)
                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + r * ld + k))
                  : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load_tile(tile);
+  load_tile(g, q);
+  uint32_t gn = g, qn = q;
+  advance(gn, qn);
   for (; tile < ntiles; tile += stride) {
-    const int64_t g = tile / nslices;
-    const int64_t q = tile - g * nslices;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
@@ -385,11 +397,11 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (tile + stride < ntiles) load_tile(tile + stride);   // next tile's loads in flight
+    if (tile + stride < ntiles) load_tile(gn, qn);          // next tile's loads in flight
 
     const int rr = lane & 15, cb = lane >> 4;
-    const int64_t r = g * 16 + rr;
-    const int64_t kb = q * 4 + cb;
+    const int64_t r = (int64_t)g * 16 + rr;
+    const int64_t kb = (int64_t)q * 4 + cb;
     const bool valid = r < rows && (kb << 5) < cols;
     float y[32];
 #pragma unroll
@@ -435,14 +447,17 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
       s = 0u;
     }
     if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
-      uint8_t *tp = codes + tile * 2048 + cb * 512 + rr * 16;
+      uint8_t *tp = codes + (size_t)tile * 2048 + cb * 512 + rr * 16;
       *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
       *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
     } else {
-      *reinterpret_cast<uint4 *>(codes + tile * 1024 + lane * 16) =
+      *reinterpret_cast<uint4 *>(codes + (size_t)tile * 1024 + lane * 16) =
           make_uint4(out[0], out[1], out[2], out[3]);
     }
     scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
+    g = gn;
+    q = qn;
+    advance(gn, qn);
     __builtin_amdgcn_wave_barrier();        // all lanes done with st before it is rewritten
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
