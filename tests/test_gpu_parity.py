@@ -70,9 +70,12 @@ def test_quantize_strided_input(mx, axis):
 
 @pytest.mark.parametrize("axis", [1, 0])
 @pytest.mark.parametrize("rot", ("none", "hadamard", "hadamard16"))
-def test_quantize_every_bf16_pattern(mx, axis, rot):
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_every_bf16_pattern(mx, axis, rot, rnd):
     """All 65536 bf16 bit patterns (NaN/Inf/subnormal included), plus every
-    pattern again with a 7.97 anchor leading each block."""
+    pattern again with a 7.97 anchor leading each block; both roundings (the
+    stochastic one puts every E2M1 interval and its subnormal range under
+    the Philox draws)."""
     allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     blocks = allv.reshape(2048, 32)
     n_anch = -(-65536 // 31)
@@ -82,9 +85,10 @@ def test_quantize_every_bf16_pattern(mx, axis, rot):
     x = np.concatenate([blocks, anch], 0)
     if axis == 0:
         x = np.ascontiguousarray(x.T)
-    q = mx.quantize(to_dev(x), axis=axis, rotate=rot, round="rne")
+    q = mx.quantize(to_dev(x), axis=axis, rotate=rot, round=rnd, seed=0x5EED)
     _sync()
-    _check_q(q, oracle.quantize_ref(x, axis, rotate=rot), f"axis={axis} rot={rot}")
+    _check_q(q, oracle.quantize_ref(x, axis, rotate=rot, rounding=rnd, seed=0x5EED),
+             f"axis={axis} rot={rot} rnd={rnd}")
 
 
 @pytest.mark.parametrize("rot", ROTS)
