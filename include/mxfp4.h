@@ -100,15 +100,17 @@ typedef enum mx_out_dtype { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out_dtype;
  *           bytes at c * 256 + r * 16, two codes per byte, the even K index in
  *           the low nibble. Code = sign << 3 | E2M1 magnitude code (0..7 for
  *           0, 0.5, 1, 1.5, 2, 3, 4, 6).
- *   scales: MNp * Kp / 32 bytes, [Kp/128][MNp/256][16][4][16]: the E8M0
+ *   scales: MNp * Kp / 32 bytes, [Kp/128][MNp/256][4][4][16][4]: the E8M0
  *           code s (value 2^(s-127)) of block kb = 4q + c of row
  *           mn = 256T + 16h + r is at byte
- *           ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h. One 1 KB block per
- *           K slice and 256-row panel; inside it, for a fixed (r, c), the
- *           scales of the panel's 16 row groups are 16 consecutive bytes, so
- *           the scales a matrix-instruction lane needs for consecutive row
- *           groups are consecutive bytes of one register (picked by the
- *           instruction's byte select). 0xFF marks a block that held a NaN or
+ *           (q * MNp/256 + T) * 1024 + (h / 4) * 256 + c * 64 + r * 4 + h % 4.
+ *           One 1 KB block per K slice and 256-row panel; inside it, the
+ *           256-byte quarter h / 4 holds, for every (r, c), the scales of
+ *           four consecutive row groups as four consecutive bytes at
+ *           (16c + r) * 4, so a matrix-instruction lane reads the scales of
+ *           its row groups with one linear 4-byte-per-lane read and picks
+ *           each with the instruction's byte select. 0xFF marks a block that
+ *           held a NaN or
  *           Inf (its codes are 0).
  * Padding rows and blocks hold the encoding of zeros (codes 0, scale code 0).
  * Element value = (-1)^sign * E2M1(mag) * 2^(s - 127).

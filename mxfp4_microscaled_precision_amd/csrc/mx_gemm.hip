@@ -58,8 +58,9 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, v4f c, u
 // Operands are in the tiled layout the quantizer writes: a 1 KB tile holds 16
 // rows x 128 K elements as [32-block c][row r][16 B], which is exactly the
 // 16x16x128 MFMA fragment with lane l's 16 bytes at offset 16 l; the scales
-// of a 128-wide K slice and a 256-row panel are one contiguous 1 KB block in
-// which lane (r, c) finds the 16 row groups' bytes of row r, block c. K
+// of a 128-wide K slice and a 256-row panel are one contiguous 1 KB block
+// whose 256-byte quarter hq holds, at 4 l, the scales of row groups
+// 4 hq .. 4 hq + 3 for lane l's (row l % 16, block l / 16). K
 // advances one slice per stage through a ring of four LDS stage buffers with
 // three stages in flight. Every copy is a direct-to-LDS load of one
 // contiguous 1 KB span (a code tile or a scale block), and every LDS fragment
@@ -148,7 +149,8 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, const uint8_t *
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
     const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + sb_off);
-    const uint2 sa = *reinterpret_cast<const uint2 *>(base + sa_off);
+    const uint2 sa = make_uint2(*reinterpret_cast<const uint32_t *>(base + sa_off),
+                                *reinterpret_cast<const uint32_t *>(base + sa_off + 256));
     af[0] = *reinterpret_cast<const uint4 *>(base + a_off);
     af[1] = *reinterpret_cast<const uint4 *>(base + a_off + 1024);
     // rows of 4 MFMAs, A fragments two rows ahead
@@ -214,10 +216,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   if (producer) {
     // Producer p copies row groups 4p .. 4p + 3 of A and of B (eight 1 KB
     // tiles); producer 0 also copies the stage's A scales and producer 1 its
-    // B scales: the 1 KB block of (K slice, 256-row panel), in which lane
-    // l = 4 r + c takes the 16 bytes of row-in-group r, block c for the
-    // panel's 16 row groups. Stages past the last one read zeros so the
-    // counts stay uniform.
+    // B scales: the 1 KB block of (K slice, 256-row panel), copied whole.
+    // Stages past the last one read zeros so the counts stay uniform.
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
@@ -285,12 +285,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
                       ((g.ldc & 3) == 0);
   const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
-  // scales: slot 4 lr + lg holds the 16 row groups' bytes of row-in-group lr,
-  // block lg; this wave's A rows are groups 8 wm .. 8 wm + 7, its B rows
-  // groups 4 wn .. 4 wn + 3
-  const uint32_t s_slot = (uint32_t)((lr * 4 + lg) * 16);
-  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + s_slot + wm * 8;
-  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + s_slot + wn * 4;
+  // scales: the 256 B at quarter hq of a scale block hold byte hq * 4 + j
+  // (row group) of every lane's (row lr, block lg) at lane * 4, so each read
+  // is one linear 256-byte span; this wave's A rows are groups
+  // 8 wm .. 8 wm + 7 (quarters 2 wm, 2 wm + 1), its B rows groups
+  // 4 wn .. 4 wn + 3 (quarter wn)
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + wm * 512 + lane * 4;
+  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + wn * 256 + lane * 4;
   if (wm == 1)
     consumer_loop<OUT_BF16, true>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, line_ok,
                                   a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);

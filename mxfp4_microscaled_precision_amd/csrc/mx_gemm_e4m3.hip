@@ -174,9 +174,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
   uint8_t *slab = smem + kRing * kStageBytes + wave * kSlab;
   const uint32_t a_off = (uint32_t)((wm * 8) * 2048 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 2048 + lane * 16);
-  const uint32_t s_slot = (uint32_t)((lr * 4 + lg) * 16);
-  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + s_slot + wm * 8;
-  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + 1024) + s_slot + wn * 4;
+  // scales: the 256 B at quarter hq of a scale block hold byte hq * 4 + j
+  // (row group) of every lane's (row lr, block lg) at lane * 4, so each read
+  // is one linear 256-byte span; this wave's A rows are groups
+  // 8 wm .. 8 wm + 7 (quarters 2 wm, 2 wm + 1), its B rows groups
+  // 4 wn .. 4 wn + 3 (quarter wn)
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + wm * 512 + lane * 4;
+  const uint32_t sb_off = (uint32_t)(kStageA + kStageB + 1024) + wn * 256 + lane * 4;
   v4f acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -196,7 +200,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = load_frag(base + b_off + j * 2048);
     const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + sb_off);
-    const uint2 sa = *reinterpret_cast<const uint2 *>(base + sa_off);
+    const uint2 sa = make_uint2(*reinterpret_cast<const uint32_t *>(base + sa_off),
+                                *reinterpret_cast<const uint32_t *>(base + sa_off + 256));
     af[0] = load_frag(base + a_off);
     consume_rows(std::make_integer_sequence<int, 8>{}, acc, bf, af, base + a_off, sb, sa, copy);
     if (more) advance();

@@ -309,9 +309,9 @@ __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_
 // reduction-major, [MN, K], zero-padded to [MNp, Kp] (MNp multiple of 256, Kp
 // of 128). Codes: tile (g, q) = rows 16g.., K elements 128q.. is 1 KB at
 // (g * Kp/128 + q) * 1024, block c of row r at c * 256 + r * 16 inside it.
-// Scales: [Kp/128][MNp/256][16][4][16], the scale of row 256T + 16h + r,
-// block 4q + c at ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h. Padding
-// positions hold the encoding of zeros (codes 0, scale code 0).
+// Scales: [Kp/128][MNp/256][4][4][16][4], the scale of row 256T + 16h + r,
+// block 4q + c at (q * MNp/256 + T) * 1024 + (h / 4) * 256 + c * 64 + r * 4 +
+// h % 4. Padding positions hold the encoding of zeros (codes 0, scale code 0).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t code_offset(int64_t mn, int64_t kb, int64_t nslices) {
   return ((mn >> 4) * nslices + (kb >> 2)) * 1024 + (kb & 3) * 256 + (mn & 15) * 16;
@@ -325,8 +325,9 @@ __device__ __forceinline__ int64_t code_offset_e4m3(int64_t mn, int64_t kb, int6
   return ((mn >> 4) * nslices + (kb >> 2)) * 2048 + (kb & 3) * 512 + (mn & 15) * 16;
 }
 __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t mnp) {
-  return (((kb >> 2) * (mnp >> 8) + (mn >> 8)) * 16 + (mn & 15)) * 64 + (kb & 3) * 16 +
-         ((mn >> 4) & 15);
+  const int64_t h = (mn >> 4) & 15;
+  return ((kb >> 2) * (mnp >> 8) + (mn >> 8)) * 1024 + (h >> 2) * 256 + (kb & 3) * 64 +
+         (mn & 15) * 4 + (h & 3);
 }
 
 // ---------------------------------------------------------------------------

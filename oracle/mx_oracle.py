@@ -546,22 +546,23 @@ def tile_codes(codes: np.ndarray) -> np.ndarray:
 
 
 def tile_scales(scales: np.ndarray, k: int) -> np.ndarray:
-    """Scales [MN, K/32] -> tiled buffer [Kp/128][MNp/256][16][4][16] (padding
-    scale code 0, the code of an all-zero block).
+    """Scales [MN, K/32] -> tiled buffer [Kp/128][MNp/256][4][4][16][4]
+    (padding scale code 0, the code of an all-zero block).
 
     The scale of row m = 256 T + 16 h + r (panel T, row group h inside it, row
     r) and block kb = 4 q + c is the byte at
-    ((q * MNp/256 + T) * 16 + r) * 64 + c * 16 + h: one 1 KB block per K slice
-    and 256-row panel, in which the scales of the panel's 16 row groups for a
-    fixed (r, c) are 16 consecutive bytes.
+    (q * MNp/256 + T) * 1024 + (h // 4) * 256 + c * 64 + r * 4 + h % 4: one
+    1 KB block per K slice and 256-row panel; its 256-byte quarter h // 4
+    holds, for every (r, c), the scales of four consecutive row groups as 4
+    consecutive bytes at (16 c + r) * 4.
     """
     scales = np.asarray(scales, dtype=np.uint8)
     mn = scales.shape[0]
     mnp, kp = padded_extents(mn, k)
     full = np.zeros((mnp, kp // 32), np.uint8)
     full[:mn, :scales.shape[1]] = scales
-    t = full.reshape(mnp // PANEL_ROWS, PANEL_ROWS // TILE_ROWS, TILE_ROWS, kp // TILE_K, 4)  # T h r q c
-    return np.ascontiguousarray(t.transpose(3, 0, 2, 4, 1)).reshape(-1)                     # q T r c h
+    t = full.reshape(mnp // PANEL_ROWS, 4, 4, TILE_ROWS, kp // TILE_K, 4)  # T hq hl r q c
+    return np.ascontiguousarray(t.transpose(4, 0, 1, 5, 3, 2)).reshape(-1)  # q T hq c r hl
 
 
 def tile_codes_fp8(codes: np.ndarray) -> np.ndarray:
@@ -603,8 +604,8 @@ def untile_scales(buf: np.ndarray, mn: int, k: int) -> np.ndarray:
     """Inverse of tile_scales: tiled bytes -> scales [MN, K/32]."""
     mnp, kp = padded_extents(mn, k)
     t = np.asarray(buf, np.uint8)[: mnp * kp // 32].reshape(
-        kp // TILE_K, mnp // PANEL_ROWS, TILE_ROWS, 4, PANEL_ROWS // TILE_ROWS)      # q T r c h
-    return t.transpose(1, 4, 2, 0, 3).reshape(mnp, kp // 32)[:mn, : k // 32]
+        kp // TILE_K, mnp // PANEL_ROWS, 4, 4, TILE_ROWS, 4)                   # q T hq c r hl
+    return t.transpose(1, 2, 5, 4, 0, 3).reshape(mnp, kp // 32)[:mn, : k // 32]
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:

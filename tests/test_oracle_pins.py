@@ -508,7 +508,8 @@ def test_tiled_layout_addresses_and_roundtrip():
                 assert nib == codes[m, kk]
             for kb in range(k // 32):
                 T, h, r, q, c = m // 256, (m // 16) % 16, m % 16, kb // 4, kb % 4
-                assert sb[((q * NT + T) * 16 + r) * 64 + c * 16 + h] == scales[m, kb]
+                assert sb[(q * NT + T) * 1024 + (h // 4) * 256 + c * 64 + r * 4 + h % 4] == \
+                    scales[m, kb]
         # padding: zero codes, scale code 0
         full = oracle.untile_codes(tb, mnp, kp)
         assert np.all(full[mn:] == 0) and np.all(full[:, k:] == 0)
