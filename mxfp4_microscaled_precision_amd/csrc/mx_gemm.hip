@@ -35,7 +35,6 @@ using namespace gemm;
 
 constexpr int kFmtFp4 = 4;
 
-
 // One 16x16x128 FP4 MFMA. The E8M0 scale of each operand is byte SELA / SELB
 // of the given register (the instruction's byte select).
 template <int SELA, int SELB>
@@ -128,12 +127,12 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v
 // faster on Fprop, Dgrad and Wgrad; splitting after 5 or 4 rows (more
 // fragments live across the barrier) was slower.
 template <int OUT_BF16, bool SHIFTED>
-__device__ __forceinline__ void consumer_loop(const GemmArgs &g, const uint8_t *smem, int total,
+__device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, int total,
                                               int nslices, int bid, int grid, int tm, int tn,
                                               bool vec_ok, bool line_ok, uint32_t a_off,
                                               uint32_t b_off, uint32_t sa_off, uint32_t sb_off,
                                               int lr, int lg, int wm, int wn) {
-  uint8_t *slab = const_cast<uint8_t *>(smem) + kRing * kStageBytes + (wm * 4 + wn) * kSlab;
+  uint8_t *slab = smem + kRing * kStageBytes + (wm * 4 + wn) * kSlab;
   constexpr int kSplit = 6;
   v4f acc[8][4];
 #pragma unroll
