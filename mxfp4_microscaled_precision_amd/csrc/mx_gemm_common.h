@@ -146,6 +146,11 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&ac
   asm volatile("" : "+v"(lr), "+v"(lg));
   const int lane = lg * 16 + lr;
   const int rr = lane >> 3, ch = lane & 7;                 // read-back row (of 8), chunk
+  // byte address of this lane's first 16 bytes (row row0 + rr); each further
+  // 8 rows add `step`, the fp32 halves add 128 bytes (an immediate offset)
+  constexpr int kEsize = OUT_BF16 ? 2 : 4;
+  const int64_t step = 8 * g.ldc * kEsize;
+  uint8_t *pi = reinterpret_cast<uint8_t *>(g.c) + ((row0 + rr) * g.ldc + col0) * kEsize + ch * 16;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -173,15 +178,10 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&ac
       for (int k = 0; k < 2; ++k) {
         const int r = k * 8 + rr;
         const uint4 d = *reinterpret_cast<const uint4 *>(slab + r * 128 + ((ch ^ (r & 7)) << 4));
-        const int64_t row = row0 + i * 16 + r;
-        if (OUT_BF16)
-          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col0 +
-                                     ch * 8) = d;
-        else
-          *reinterpret_cast<uint4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col0 +
-                                     h * 32 + ch * 4) = d;
+        *reinterpret_cast<uint4 *>(pi + k * step + h * 128) = d;
       }
     }
+    pi += 2 * step;
   }
 }
 
