@@ -87,13 +87,14 @@ static_assert(kRing * kStageBytes + kConsumers * kSlab <= 160 * 1024, "LDS");
 // with the clock settled; three would not fit the registers. B is the first
 // MFMA operand (its scale byte j of sb), A the second (scale byte I % 4 of
 // sa.x for rows 0..3, of sa.y for rows 4..7).
-template <int I, int S>
-__device__ __forceinline__ void consume_row(v4f (&acc)[8][4], const uint4 (&bf)[4], uint4 (&af)[8],
-                                            const uint8_t *a_base, uint32_t sb, uint2 sa) {
+template <int I, int S, int ROWS>
+__device__ __forceinline__ void consume_row(v4f (&acc)[ROWS][4], const uint4 (&bf)[4],
+                                            uint4 (&af)[ROWS], const uint8_t *a_base, uint32_t sb,
+                                            uint2 sa) {
   if (I < S) {
 #pragma unroll
-    for (int j = I + 2; j < (I == S - 1 ? 8 : I + 3); ++j)
-      if (j < 8) af[j < 8 ? j : 0] = *reinterpret_cast<const uint4 *>(a_base + j * 1024);
+    for (int j = I + 2; j < (I == S - 1 ? ROWS : I + 3); ++j)
+      if (j < ROWS) af[j < ROWS ? j : 0] = *reinterpret_cast<const uint4 *>(a_base + j * 1024);
   }
   const uint32_t sai = I < 4 ? sa.x : sa.y;
   acc[I][0] = mfma_fp4<0, I & 3>(bf[0], af[I], acc[I][0], sb, sai);
@@ -105,11 +106,12 @@ __device__ __forceinline__ void consume_row(v4f (&acc)[8][4], const uint4 (&bf)[
 
 // Rows LO .. LO + sizeof...(I) - 1 of a stage whose A fragments are all read
 // by the end of row S - 1.
-template <int LO, int S, int... I>
-__device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v4f (&acc)[8][4],
-                                             const uint4 (&bf)[4], uint4 (&af)[8],
-                                             const uint8_t *a_base, uint32_t sb, uint2 sa) {
-  (consume_row<LO + I, S>(acc, bf, af, a_base, sb, sa), ...);
+template <int LO, int S, int ROWS, int... I>
+__device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>,
+                                             v4f (&acc)[ROWS][4], const uint4 (&bf)[4],
+                                             uint4 (&af)[ROWS], const uint8_t *a_base, uint32_t sb,
+                                             uint2 sa) {
+  (consume_row<LO + I, S, ROWS>(acc, bf, af, a_base, sb, sa), ...);
 }
 
 // The consumers' stage loop. The consumers of wave row 0 wait at the barrier
@@ -126,17 +128,18 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>, v
 // barriers. Measured against all consumers waiting at every barrier: 3-5%
 // faster on Fprop, Dgrad and Wgrad; splitting after 5 or 4 rows (more
 // fragments live across the barrier) was slower.
-template <int OUT_BF16, bool SHIFTED>
+template <int OUT_BF16, bool SHIFTED, int ROWS>
 __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, int total,
                                               int nslices, int bid, int grid, int tm, int tn,
                                               bool vec_ok, bool line_ok, uint32_t a_off,
                                               uint32_t b_off, uint32_t sa_off, uint32_t sb_off,
                                               int lr, int lg, int wm, int wn) {
   uint8_t *slab = smem + kRing * kStageBytes + (wm * 4 + wn) * kSlab;
-  constexpr int kSplit = 6;
-  v4f acc[8][4];
+  constexpr int kSplit = ROWS == 8 ? 6 : 3;
+  constexpr bool kHalf = ROWS == 4;
+  v4f acc[ROWS][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < ROWS; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   if (SHIFTED) __syncthreads();                            // stage 0 landed
@@ -144,43 +147,47 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
   for (int G = 0; G < total; ++G) {
     if (!SHIFTED) __syncthreads();                         // stage G landed
     const uint8_t *base = smem + (G & 3) * kStageBytes;
-    uint4 bf[4], af[8];
+    uint4 bf[4], af[ROWS];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4 *>(base + b_off + j * 1024);
     const uint32_t sb = *reinterpret_cast<const uint32_t *>(base + sb_off);
     const uint2 sa = make_uint2(*reinterpret_cast<const uint32_t *>(base + sa_off),
-                                *reinterpret_cast<const uint32_t *>(base + sa_off + 256));
+                                ROWS == 8 ? *reinterpret_cast<const uint32_t *>(base + sa_off + 256)
+                                          : 0u);
     af[0] = *reinterpret_cast<const uint4 *>(base + a_off);
     af[1] = *reinterpret_cast<const uint4 *>(base + a_off + 1024);
     // rows of 4 MFMAs, A fragments two rows ahead
     if (!SHIFTED) {
-      consume_rows<0, 8>(std::make_integer_sequence<int, 8>{}, acc, bf, af, base + a_off, sb, sa);
+      consume_rows<0, ROWS, ROWS>(std::make_integer_sequence<int, ROWS>{}, acc, bf, af,
+                                  base + a_off, sb, sa);
     } else {
-      consume_rows<0, kSplit>(std::make_integer_sequence<int, kSplit>{}, acc, bf, af,
-                              base + a_off, sb, sa);
+      consume_rows<0, kSplit, ROWS>(std::make_integer_sequence<int, kSplit>{}, acc, bf, af,
+                                    base + a_off, sb, sa);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // all of stage G read
       __syncthreads();                                     // stage G + 1 landed
-      consume_rows<kSplit, kSplit>(std::make_integer_sequence<int, 8 - kSplit>{}, acc, bf, af,
-                                   base + a_off, sb, sa);
+      consume_rows<kSplit, kSplit, ROWS>(std::make_integer_sequence<int, ROWS - kSplit>{}, acc,
+                                         bf, af, base + a_off, sb, sa);
     }
     if (++cs == nslices) {
       cs = 0;
       int mi, ni;
-      tile_coords(bid + ck * grid, tm, tn, &mi, &ni);
+      tile_coords(g.tile_base + (kHalf ? (bid >> 1) : bid + ck * grid), tm, tn, &mi, &ni);
       ++ck;
-      const int64_t rbase = (int64_t)mi * kBM + wm * 128, cbase = (int64_t)ni * kBN + wn * 64;
-      if (line_ok && rbase + 128 <= g.M && cbase + 64 <= g.N) {
-        store_tile_lds<OUT_BF16>(g, acc, slab, rbase, cbase, lr, lg);
+      // a half tile is rows 128 (bid & 1) .. + 127 of the 256-row tile
+      const int64_t rbase = (int64_t)mi * kBM + (kHalf ? (bid & 1) * 128 : 0) + wm * (ROWS * 16);
+      const int64_t cbase = (int64_t)ni * kBN + wn * 64;
+      if (line_ok && rbase + ROWS * 16 <= g.M && cbase + 64 <= g.N) {
+        store_tile_lds<OUT_BF16, ROWS>(g, acc, slab, rbase, cbase, lr, lg);
       } else {
         const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < ROWS; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < ROWS; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
@@ -189,10 +196,17 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
 }
 
 // Persistent: one workgroup per compute unit walks the tiles bid, bid + grid,
-// ... as one continuous sequence of stages; producers run three stages ahead
-// across tile boundaries, and consumers store a finished tile while the next
-// tile's first stages are already in flight.
-template <int OUT_BF16>
+// ... of [tile_base, tile_base + tile_count) as one continuous sequence of
+// stages; producers run three stages ahead across tile boundaries, and
+// consumers store a finished tile while the next tile's first stages are
+// already in flight.
+//
+// HALF = 1 is the tail launch: workgroup bid computes half bid & 1 (rows
+// 128 (bid & 1) .. + 127) of tile tile_base + (bid >> 1), with the same
+// twelve waves: consumers on 64x64 pieces (4 rows of 4 MFMAs), producers
+// copying the half's 8 A row groups and all 16 of B. Each output element
+// sees the same MFMAs in the same order as in a whole tile.
+template <int OUT_BF16, int HALF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes + kConsumers * kSlab];
 
@@ -202,9 +216,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const bool producer = wave >= kConsumers;
   const int wm = (wave >> 2) & 1, wn = wave & 3;               // consumers: 2 x 4 grid
   const int tm = (int)((g.M + kBM - 1) / kBM), tn = (int)((g.N + kBN - 1) / kBN);
-  const int tiles = tm * tn;
   const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
-  const int ntl = (tiles - bid + grid - 1) / grid;             // tiles of this workgroup
+  const int ntl = HALF ? 1 : (g.tile_count - bid + grid - 1) / grid;   // tiles of this workgroup
+  const int half = HALF ? (bid & 1) : 0;
   const int mp = (int)((g.M + 255) & ~255LL), np = (int)((g.N + 255) & ~255LL);   // padded rows
   const int nslices = (int)((g.K + 127) >> 7);
   const int total = ntl * nslices;                             // stages of this workgroup
@@ -213,10 +227,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   const int lg = lane >> 4;      // 32-element K block within the slice
 
   if (producer) {
-    // Producer p copies row groups 4p .. 4p + 3 of A and of B (eight 1 KB
-    // tiles); producer 0 also copies the stage's A scales and producer 1 its
-    // B scales: the 1 KB block of (K slice, 256-row panel), copied whole.
-    // Stages past the last one read zeros so the counts stay uniform.
+    // Producer p copies row groups 4p .. 4p + 3 of A (2p, 2p + 1 of the
+    // half for HALF) and of B (1 KB tiles); producer 0 also copies the
+    // stage's A scales and producer 1 its B scales: the 1 KB block of (K
+    // slice, 256-row panel), copied whole. Stages past the last one read
+    // zeros so the counts stay uniform.
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
@@ -232,8 +247,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     auto set_tile = [&](int k) {
       tile_live = k < ntl;
       int mi = 0, ni = 0;
-      if (tile_live) tile_coords(bid + k * grid, tm, tn, &mi, &ni);
-      ga = mi * (kBM / 16) + p * 4;
+      if (tile_live) tile_coords(g.tile_base + (HALF ? (bid >> 1) : bid + k * grid), tm, tn, &mi, &ni);
+      ga = mi * (kBM / 16) + (HALF ? half * 8 + p * 2 : p * 4);
       gb = ni * (kBN / 16) + p * 4;
       gs = p == 0 ? mi : ni;                                   // the tile's panel
     };
@@ -248,7 +263,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) {
         const int off = (j * nslices + is) * 1024;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 4 + j) * 1024));
-        dma_load16(rsrc_a, tile_live ? al + off : a_bytes, dst);
+        if (!HALF || j < 2)
+          dma_load16(rsrc_a, tile_live ? al + off : a_bytes,
+                     HALF ? __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 2 + j) * 1024))
+                          : dst);
         dma_load16(rsrc_b, tile_live ? bl + off : b_bytes, dst + kStageA);
       }
       if (p < 2)
@@ -263,11 +281,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     for (int G = 0; G < kAhead; ++G) issue(G);
     for (int G = 0; G < total; ++G) {
       // own part of stage G landed: nine copies per stage on producers 0
-      // and 1, eight on 2 and 3, two later stages outstanding
-      if (p < 2)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      // and 1, eight on 2 and 3 (seven and six for HALF), two later stages
+      // outstanding
+      if (HALF) {
+        if (p < 2)
+          asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      } else {
+        if (p < 2)
+          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      }
       __syncthreads();                                     // stage G visible; G - 1 free
       issue((G + kAhead) & 3);
     }
@@ -282,21 +308,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
                        ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) &&
                       ((g.ldc & 3) == 0);
-  const uint32_t a_off = (uint32_t)((wm * 8) * 1024 + lane * 16);
+  constexpr int kRows = HALF ? 4 : 8;                          // MFMA rows per consumer
+  const uint32_t a_off = (uint32_t)((wm * kRows) * 1024 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
   // scales: the 256 B at quarter hq of a scale block hold byte hq * 4 + j
   // (row group) of every lane's (row lr, block lg) at lane * 4, so each read
   // is one linear 256-byte span; this wave's A rows are groups
-  // 8 wm .. 8 wm + 7 (quarters 2 wm, 2 wm + 1), its B rows groups
+  // 8 wm .. 8 wm + 7 (quarters 2 wm, 2 wm + 1; for HALF, groups
+  // 8 half + 4 wm .. + 3, quarter 2 half + wm), its B rows groups
   // 4 wn .. 4 wn + 3 (quarter wn)
-  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) + wm * 512 + lane * 4;
+  const uint32_t sa_off = (uint32_t)(kStageA + kStageB) +
+                          (HALF ? (2 * half + wm) * 256 : wm * 512) + lane * 4;
   const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + wn * 256 + lane * 4;
   if (wm == 1)
-    consumer_loop<OUT_BF16, true>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, line_ok,
-                                  a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
+    consumer_loop<OUT_BF16, true, kRows>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
+                                         line_ok, a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
   else
-    consumer_loop<OUT_BF16, false>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok, line_ok,
-                                   a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
+    consumer_loop<OUT_BF16, false, kRows>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
+                                          line_ok, a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
 }
 
 template <int OUT_BF16>
@@ -336,9 +365,26 @@ hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
                       : launch(fill_zero_kernel<0>, grid, dim3(256), 0, stream, g);
   }
   const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
-  const dim3 grid((unsigned)std::min<int64_t>(tiles, cu_count()));
-  return g.out_bf16 ? launch(gemm_tiled_kernel<1>, grid, dim3(kThreads), 0, stream, g)
-                    : launch(gemm_tiled_kernel<0>, grid, dim3(kThreads), 0, stream, g);
+  const int64_t cus = cu_count();
+  // When the last round of whole tiles would fill at most half the compute
+  // units (e.g. 896 tiles = 3.5 rounds on 256), the whole rounds run first
+  // and the leftover tiles then run as twice as many half tiles, one per
+  // workgroup.
+  const int64_t rem = tiles % cus;
+  const bool split = tiles > cus && rem != 0 && 2 * rem <= cus;
+  GemmArgs a = g;
+  a.tile_base = 0;
+  a.tile_count = (int)(split ? tiles - rem : tiles);
+  const dim3 grid((unsigned)std::min<int64_t>(a.tile_count, cus));
+  hipError_t e = g.out_bf16 ? launch(gemm_tiled_kernel<1, 0>, grid, dim3(kThreads), 0, stream, a)
+                            : launch(gemm_tiled_kernel<0, 0>, grid, dim3(kThreads), 0, stream, a);
+  if (e != hipSuccess || !split) return e;
+  GemmArgs h = g;
+  h.tile_base = a.tile_count;
+  h.tile_count = (int)rem;
+  const dim3 hgrid((unsigned)(2 * rem));
+  return g.out_bf16 ? launch(gemm_tiled_kernel<1, 1>, hgrid, dim3(kThreads), 0, stream, h)
+                    : launch(gemm_tiled_kernel<0, 1>, hgrid, dim3(kThreads), 0, stream, h);
 }
 
 }  // namespace mx

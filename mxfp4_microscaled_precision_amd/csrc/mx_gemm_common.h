@@ -124,7 +124,7 @@ __device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc
 
 constexpr int kSlab = 2048;                        // epilogue staging per 128x64 wave tile
 
-// Stores a finished 128x64 wave tile (rows row0.., columns col0..) through
+// Stores a finished (16 ROWS)x64 wave tile (rows row0.., columns col0..) through
 // the wave's private 2 KB LDS slab, 16 rows at a time: lane (lr, lg) writes
 // its quads of row lr, then lane l reads back 16 contiguous bytes of row
 // l / 8 (chunk l % 8) and stores them, so that each store instruction
@@ -136,8 +136,8 @@ constexpr int kSlab = 2048;                        // epilogue staging per 128x6
 // identical output): Fprop 70.7 -> 61.0 us, Dgrad 236 -> 204 us, Wgrad (fp32
 // out) 228 -> 222 us. Wave tiles that cross the edge of C, or a C that is not
 // 16-byte aligned, keep the quad stores.
-template <int OUT_BF16>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&acc)[8][4],
+template <int OUT_BF16, int ROWS>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&acc)[ROWS][4],
                                                uint8_t *slab, int64_t row0, int64_t col0, int lr,
                                                int lg) {
   // Opaque copies: keeps the compiler from hoisting these lane addresses
@@ -152,7 +152,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&ac
   const int64_t step = 8 * g.ldc * kEsize;
   uint8_t *pi = reinterpret_cast<uint8_t *>(g.c) + ((row0 + rr) * g.ldc + col0) * kEsize + ch * 16;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < ROWS; ++i) {
 #pragma unroll
     for (int h = 0; h < (OUT_BF16 ? 1 : 2); ++h) {
       if (OUT_BF16) {

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
       ++ck;
       const int64_t rbase = (int64_t)mi * kBM + wm * 128, cbase = (int64_t)ni * kBN + wn * 64;
       if (line_ok && rbase + 128 <= g.M && cbase + 64 <= g.N) {
-        store_tile_lds<OUT_BF16>(g, acc, slab, rbase, cbase, lr, lg);
+        store_tile_lds<OUT_BF16, 8>(g, acc, slab, rbase, cbase, lr, lg);
       } else {
         const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
 #pragma unroll

@@ -62,6 +62,9 @@ struct GemmArgs {
   void *c;                            // [M][N], leading dimension ldc
   int64_t M, N, K, ldc;
   int out_bf16;
+  // Set by the launcher: the output tiles (in its ordering) one launch of
+  // the MXFP4 GEMM covers, [tile_base, tile_base + tile_count).
+  int tile_base, tile_count;
 };
 
 hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream);

@@ -236,6 +236,33 @@ def test_gemm_lds_path_tails(mx, M, N, K):
     _gemm_case(mx, "fprop", A, B, "hadamard", "rne", 0)
 
 
+@pytest.mark.parametrize("op", ["fprop", "wgrad"])
+def test_gemm_tail_half_tiles(mx, op):
+    """5 x 60 = 300 output tiles of 256 x 256: on a 256-compute-unit MI355X the
+    launcher runs 256 whole tiles, then the other 44 as 88 half tiles (rows
+    128 h .. 128 h + 127 of a tile). Ragged in M, N and K; both output dtypes
+    against the oracle, and a misaligned output pitch (the per-quad stores
+    inside the half tiles) equal bit for bit to the contiguous result."""
+    import torch
+    rng = np.random.default_rng(404)
+    M, N, K = 1243, 15355, 224
+    if op == "fprop":                                  # X [T=M, in=K], W [out=N, in=K]
+        a, b = _rand_bits(rng, (M, K)), _rand_bits(rng, (N, K), 0.02)
+    else:                                              # dY [T=K, out=M], X [T=K, in=N]
+        a, b = _rand_bits(rng, (K, M), 1e-2), _rand_bits(rng, (K, N))
+    _gemm_case(mx, op, a, b, "hadamard", "rne", 0)
+    ax_a, ax_b = mx.OP_AXES[op]
+    qa = mx.quantize(to_dev(a), ax_a, "hadamard", "rne", seed=0)
+    qb = mx.quantize(to_dev(b), ax_b, "hadamard", "rne", seed=1 << 32)
+    for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        ref = mx.linear(op, qa, qb, dt)
+        big = torch.full((M, N + 3), 7.0, dtype=tdt, device="cuda")
+        mx.linear(op, qa, qb, dt, out=big[:, :N])
+        _sync()
+        assert torch.equal(big[:, :N], ref), f"{op} {dt}: strided output differs"
+        assert torch.all(big[:, N:] == 7.0), f"{op} {dt}: pad columns written"
+
+
 def test_gemm_several_tiles(mx):
     rng = np.random.default_rng(22)
     A = _rand_bits(rng, (640, 1024))
