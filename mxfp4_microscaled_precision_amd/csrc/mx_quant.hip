@@ -341,7 +341,7 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 // 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging writes
 // and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
 // ---------------------------------------------------------------------------
-constexpr int kAxis1WgPerCu = 4;   // 16 waves per compute unit (measured best of 2, 4, 8)
+constexpr int kAxis1WgPerCu = 3;   // 12 waves per compute unit (measured best of 2, 3, 4, 6, 8)
 
 template <int ROT, int RND, int FMT>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(

@@ -399,6 +399,18 @@ def test_quantize_axis1_many_tiles_ragged(mx):
     assert np.array_equal(host_u8(q8.scales), oracle.tile_scales(ref8.scales, 2048))
 
 
+def test_quantize_axis1_walk_with_slice_wrap(mx):
+    """20000 x 608: 5 K slices (the last one ragged) and 6320 tiles, more than
+    the resident waves, and a wave stride that is not a multiple of 5, so each
+    wave's (row group, K slice) pair wraps the slice index as it walks; every
+    byte checked."""
+    rng = np.random.default_rng(62)
+    x = _rand_bits(rng, (20000, 608))
+    q = mx.quantize(to_dev(x), axis=1, rotate="hadamard", round="rne")
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, 1, rotate="hadamard"), "walk with slice wrap")
+
+
 @pytest.mark.parametrize("rot", ROTS)
 @pytest.mark.parametrize("shape,ld", [((160, 100), 100), ((256, 64), 64), ((96, 516), 520),
                                       ((32, 4), 8)])
