@@ -367,17 +367,20 @@ hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
   const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
   const int64_t cus = cu_count();
   // When the last round of whole tiles would fill at most half the compute
-  // units (e.g. 896 tiles = 3.5 rounds on 256), the whole rounds run first
-  // and the leftover tiles then run as twice as many half tiles, one per
-  // workgroup.
+  // units (e.g. 896 tiles = 3.5 rounds on 256, or 64 tiles in all), the
+  // whole rounds run first and the leftover tiles then run as twice as many
+  // half tiles, one per workgroup.
   const int64_t rem = tiles % cus;
-  const bool split = tiles > cus && rem != 0 && 2 * rem <= cus;
+  const bool split = rem != 0 && 2 * rem <= cus;
   GemmArgs a = g;
   a.tile_base = 0;
   a.tile_count = (int)(split ? tiles - rem : tiles);
-  const dim3 grid((unsigned)std::min<int64_t>(a.tile_count, cus));
-  hipError_t e = g.out_bf16 ? launch(gemm_tiled_kernel<1, 0>, grid, dim3(kThreads), 0, stream, a)
-                            : launch(gemm_tiled_kernel<0, 0>, grid, dim3(kThreads), 0, stream, a);
+  hipError_t e = hipSuccess;
+  if (a.tile_count > 0) {
+    const dim3 grid((unsigned)std::min<int64_t>(a.tile_count, cus));
+    e = g.out_bf16 ? launch(gemm_tiled_kernel<1, 0>, grid, dim3(kThreads), 0, stream, a)
+                   : launch(gemm_tiled_kernel<0, 0>, grid, dim3(kThreads), 0, stream, a);
+  }
   if (e != hipSuccess || !split) return e;
   GemmArgs h = g;
   h.tile_base = a.tile_count;

@@ -237,15 +237,18 @@ def test_gemm_lds_path_tails(mx, M, N, K):
 
 
 @pytest.mark.parametrize("op", ["fprop", "wgrad"])
-def test_gemm_tail_half_tiles(mx, op):
-    """5 x 60 = 300 output tiles of 256 x 256: on a 256-compute-unit MI355X the
-    launcher runs 256 whole tiles, then the other 44 as 88 half tiles (rows
-    128 h .. 128 h + 127 of a tile). Ragged in M, N and K; both output dtypes
-    against the oracle, and a misaligned output pitch (the per-quad stores
-    inside the half tiles) equal bit for bit to the contiguous result."""
+@pytest.mark.parametrize("M,N", [(1243, 15355), (2148, 4133), (1000, 900)])
+def test_gemm_launch_paths(mx, op, M, N):
+    """The launcher's three paths on a 256-compute-unit MI355X (tiles of
+    256 x 256): 1243 x 15355 is 300 tiles, 256 whole ones then the other 44 as
+    88 half tiles (rows 128 h .. 128 h + 127 of a tile); 2148 x 4133 is 153
+    whole tiles; 1000 x 900 is 16 tiles, all run as 32 half tiles. Ragged in
+    M, N and K (224); both output dtypes against the oracle, and a misaligned
+    output pitch (the per-quad stores) equal bit for bit to the contiguous
+    result."""
     import torch
-    rng = np.random.default_rng(404)
-    M, N, K = 1243, 15355, 224
+    rng = np.random.default_rng(404 + M)
+    K = 224
     if op == "fprop":                                  # X [T=M, in=K], W [out=N, in=K]
         a, b = _rand_bits(rng, (M, K)), _rand_bits(rng, (N, K), 0.02)
     else:                                              # dY [T=K, out=M], X [T=K, in=N]
