@@ -592,22 +592,88 @@ def structural_error(mx, T=8192, n_out=2048, n_in=1024, steps=64, data_seed=3):
 SHARED_INPUT_LINEARS = ("k_proj", "v_proj", "up_proj")
 
 
+def block_dual_linear(mx, wl, tensors, steps):
+    """One linear of the block as a training step runs it with the dual-output
+    quantizer: X, W and dY are each quantized once into both orientations
+    (mx_quantize_dual), then Fprop, Dgrad and Wgrad run on those operands.
+    The operands are byte for byte those of the per-op quantizations. Returns
+    {variant: ms per linear}."""
+    import numpy as np
+    import torch
+    lib = mx.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+
+    src = {k: dev(tensors[k]) for k in ("X", "W", "dY")}
+    T, n_out, n_in = wl.tokens, wl.out_features, wl.in_features
+    bufs, descs = {}, {}
+    for k, x in src.items():
+        rows, cols = x.shape
+        for axis in (1, 0):
+            cb, sb = mx.quantize_sizes(rows, cols, axis)
+            bufs[k, axis] = (torch.empty(cb, dtype=torch.uint8, device="cuda"),
+                             torch.empty(sb, dtype=torch.uint8, device="cuda"))
+            descs[k, axis] = mx.QTensorDesc()
+    outs = {"fprop": torch.empty((T, n_out), dtype=torch.bfloat16, device="cuda"),
+            "dgrad": torch.empty((T, n_in), dtype=torch.bfloat16, device="cuda"),
+            "wgrad": torch.empty((n_out, n_in), dtype=torch.float32, device="cuda")}
+    # (A, B) of each op, as (tensor, axis)
+    ops = {"fprop": (("X", 1), ("W", 1)), "dgrad": (("dY", 1), ("W", 0)),
+           "wgrad": (("dY", 0), ("X", 0))}
+    res = {}
+    for label, rot, rnd, seed in wl.variants:
+        sa = seed & 0xFFFFFFFF
+        sb_ = sa | (1 << 32)
+        # seeds by role: X is A of Fprop and B of Wgrad; W is B of both of
+        # its ops; dY is A of both of its ops
+        seeds = {"X": (sa, sb_), "W": (sb_, sb_), "dY": (sa, sa)}
+
+        def step(i):
+            for k, x in src.items():
+                s1, s0 = seeds[k]
+                if lib.mx_quantize_dual(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), 32,
+                                        mx.ROTATE[rot], mx.ROUND[rnd], s1, s0,
+                                        bufs[k, 1][0].data_ptr(), bufs[k, 1][1].data_ptr(),
+                                        bufs[k, 0][0].data_ptr(), bufs[k, 0][1].data_ptr(),
+                                        ctypes.byref(descs[k, 1]), ctypes.byref(descs[k, 0]), st):
+                    raise RuntimeError("mx_quantize_dual failed")
+            for op, (a, b) in ops.items():
+                c = outs[op]
+                if lib.mx_linear(mx.OPS[op], ctypes.byref(descs[a]), ctypes.byref(descs[b]),
+                                 c.data_ptr(), c.stride(0), 1 if op != "wgrad" else 0, st):
+                    raise RuntimeError("mx_linear failed")
+
+        res[label] = time_loop(step, steps)
+    del src, bufs, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_block(mx, wls, steps):
     """Full Llama-3.1-8B block: 7 linears x {fprop, dgrad, wgrad} per variant.
 
     Each op quantizes its own two operands (the primary figure). The
     `shared_input` figure also drops the X quantizations that k/v reuse from
-    q and up from gate, using the same measured per-kernel times."""
+    q and up from gate, using the same measured per-kernel times. The
+    `dual_quantizer` figure times each linear as a training step runs it:
+    X, W and dY quantized once each into both orientations, then the three
+    GEMMs (block_dual_linear)."""
     import torch
     from datagen import workload_tensors
     res = {}
     cache = {}
+    dual_ms = {}
     for wl in wls:
         key = wl.data_seed
         if key not in cache:
             cache.clear()
             torch.cuda.empty_cache()
             cache[key] = workload_tensors(wl)
+            for v, ms in block_dual_linear(mx, wl, cache[key], steps).items():
+                dual_ms[v] = dual_ms.get(v, 0.0) + ms
         for v in wl.variants:
             rr = Runner(mx, wl, v[0], tensors=cache[key], min_bytes=0)
             m = measure(rr, steps)
@@ -627,6 +693,11 @@ def bench_block(mx, wls, steps):
         ms_shared = d["ms"] - d.pop("saved_ms")
         d["shared_input"] = {"ms": round(ms_shared, 4),
                              "tflops": round(d["flops"] / (ms_shared * 1e-3) / 1e12, 2)}
+        if v in dual_ms:
+            d["dual_quantizer"] = {"ms": round(dual_ms[v], 4),
+                                   "tflops": round(d["flops"] / (dual_ms[v] * 1e-3) / 1e12, 2),
+                                   "pct_mfma_peak": round(100 * d["flops"] / (dual_ms[v] * 1e-3)
+                                                          / 1e12 / PEAK_FP4_TFLOPS, 2)}
     return res
 
 

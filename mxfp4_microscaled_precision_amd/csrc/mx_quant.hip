@@ -304,6 +304,27 @@ __device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_
   }
 }
 
+// Sign bits of K indices 4 ctr .. 4 ctr + 3 as a nibble (bit j for index
+// 4 ctr + j), from one Philox call of the sign stream.
+__device__ __forceinline__ uint32_t sign_nibble(uint32_t ctr, uint32_t seed_lo) {
+  const U4 sw = sign_words(ctr, seed_lo);
+  return (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
+}
+
+// The 32 sign bits whose nibbles lanes base .. base + 7 of the wave hold
+// (bit i for element i of the block).
+__device__ __forceinline__ uint32_t gather_sign_mask(uint32_t nib, int base) {
+  uint32_t mask = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mask |= (uint32_t)__builtin_amdgcn_readlane((int)nib, base + j) << (4 * j);
+  return mask;
+}
+
+__device__ __forceinline__ void apply_sign_mask(float (&y)[32], uint32_t mask) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
+}
+
 // ---------------------------------------------------------------------------
 // Output layout (tiled, see mx_qtensor in mxfp4.h): the operand is viewed
 // reduction-major, [MN, K], zero-padded to [MNp, Kp] (MNp multiple of 256, Kp
@@ -705,11 +726,22 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
   float y[32];
   uint32_t out[4];
   uint32_t s;
+  const int lane = tid & 63;
   if (tid < 128) {
     // axis 1: row R0 + rr (< mnp1), 32-block kb along the columns
     const int rr = tid & 31, b = tid >> 5;
     const int64_t r = R0 + rr;
     const int64_t kb = (C0 >> 5) + b;
+    // random signs: this wave's two blocks need the 16 sign calls at
+    // counters ((C0 / 32) + 2 wave) * 8 + m, m < 16; lane m makes call m
+    // (before any lane leaves, so that every source lane is active)
+    uint32_t mask = 0u;
+    if (ROT == MX_K_ROT_RAND_SIGN) {
+      const uint32_t nib =
+          sign_nibble((uint32_t)(((C0 >> 5) + 2 * (tid >> 6)) * 8 + (lane & 15)), s1_lo);
+      const uint32_t m0 = gather_sign_mask(nib, 0), m1 = gather_sign_mask(nib, 8);
+      mask = (lane >> 5) ? m1 : m0;
+    }
     if (kb >= nsl1 * 4) return;                           // past the operand's K extent
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -720,7 +752,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
         y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
       }
     }
-    if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)(kb << 5), s1_lo);
+    if (ROT == MX_K_ROT_RAND_SIGN) apply_sign_mask(y, mask);
     rotate_block<ROT>(y);
     const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;   // L % 4 == 0
     U4 w{0u, 0u, 0u, 0u};
@@ -742,21 +774,64 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(
     const int cc = tid - 128;
     const int64_t c = C0 + cc;                            // < mnp0
     const int64_t kb = R0 >> 5;
-    if (kb >= nsl0 * 4) return;                           // past the operand's K extent
-    if (rows_live && c < cols) {
+    if (kb >= nsl0 * 4) return;                           // past the operand's K extent (uniform)
+    // random signs: the block's 32 rows need the 8 sign calls at counters
+    // R0 / 4 + j; lane j makes call j
+    uint32_t mask = 0u;
+    if (ROT == MX_K_ROT_RAND_SIGN)
+      mask = gather_sign_mask(sign_nibble((uint32_t)((R0 >> 2) + (lane & 7)), s0_lo), 0);
+    if (rows_live && c < cols) {                          // uniform over each quad (cols % 32 == 0)
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const uint16_t bits =
             *reinterpret_cast<const uint16_t *>(st + j * 256 + (((cc >> 3) ^ (j & 15)) << 4) + (cc & 7) * 2);
         y[j] = bits_f((uint32_t)bits << 16);
       }
-      if (ROT == MX_K_ROT_RAND_SIGN) apply_signs(y, (uint32_t)R0, s0_lo);
+      if (ROT == MX_K_ROT_RAND_SIGN) apply_sign_mask(y, mask);
       rotate_block<ROT>(y);
-      auto u24_of = [&](int i) -> uint32_t {
-        const uint64_t L = (uint64_t)((R0 + i) * cols + c);
-        return pick_word(sr_words(L >> 2, s0_lo, s0_hi), (uint32_t)(L & 3)) >> 8;
-      };
-      s = quantize_block<RotKind<ROT>::value, RND, kFmtE2M1>(y, out, u24_of);
+      if (RND == MX_K_ROUND_SR) {
+        // element (R0 + i, c) draws word c % 4 of the call at
+        // ((R0 + i) cols + c - c % 4) / 4 (cols % 4 == 0): the four lanes of
+        // a quad (columns 4m .. 4m + 3) share each call. Lane q makes the
+        // calls of rows i + q and a 4 x 4 transpose over DPP hands each lane
+        // its column's words, as in quant_axis0_sr_kernel.
+        float m1, m2;
+        s = block_scale<RotKind<ROT>::value>(y, m1, m2);
+        const uint32_t q = (uint32_t)(cc & 3);
+        const uint64_t lq0 = (uint64_t)R0 * (uint64_t)cols + (uint64_t)(c & ~(int64_t)3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+          const U4 w = sr_words((lq0 + (uint64_t)(i + (int)q) * (uint64_t)cols) >> 2, s0_lo,
+                                s0_hi);
+          const uint32_t own = pick_word(w, q);
+          const uint32_t g1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick_word(w, q ^ 1u),
+                                                                    0xB1, 0xF, 0xF, false);
+          const uint32_t g2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick_word(w, q ^ 2u),
+                                                                    0x4E, 0xF, 0xF, false);
+          const uint32_t g3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick_word(w, q ^ 3u),
+                                                                    0x1B, 0xF, 0xF, false);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t d = (uint32_t)r ^ q;           // row i + r came from lane q ^ d
+            uint32_t u = own;
+            u = d == 1u ? g1 : u;
+            u = d == 2u ? g2 : u;
+            u = d == 3u ? g3 : u;
+            const uint32_t t = f_bits(__fmul_rn(__fmul_rn(y[i + r], m1), m2));
+            out[(i + r) >> 3] |= (e2m1_sr_mag(t & 0x7FFFFFFFu, u >> 8) | ((t >> 28) & 8u))
+                                 << (4 * ((i + r) & 7));
+          }
+        }
+        if (s == 0xFFu) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) out[j] = 0u;
+        }
+      } else {
+        auto u24_of = [](int) -> uint32_t { return 0u; };   // nearest rounding draws nothing
+        s = quantize_block<RotKind<ROT>::value, RND, kFmtE2M1>(y, out, u24_of);
+      }
     } else {                                              // K padding of the operand
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = 0u;
