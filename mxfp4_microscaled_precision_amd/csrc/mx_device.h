@@ -112,29 +112,22 @@ __device__ __forceinline__ uint32_t e2m1_rne_mag(uint32_t ab) {
 
 // Stochastic E2M1 magnitude code: lo <= a < hi neighbours, upper one taken
 // when u24 < f * 2^24 with f = (a - lo) / (hi - lo); a >= 6 gives 6 (not
-// randomised). Read off the fp32 bits of a (biased exponent eb, mantissa m):
-//  * 1 <= a < 6 (eb 127..129): the gap is 2^(eb - 128), lo has code
-//    2 (eb - 126) + (top mantissa bit), and f * 2^24 = (m mod 2^22) * 4;
-//  * 0.5 <= a < 1 (eb 126): lo = 0.5 (code 1), gap 0.5, f * 2^24 = m * 2;
-//  * a < 0.5: lo = 0, gap 0.5, f * 2^24 = a * 2^25, exact in fp32, and for
-//    an integer u24, u24 < a * 2^25 exactly when u24 < ceil(a * 2^25).
-// So one integer threshold below 2^24 serves every region, and the choice
-// is the sign bit of u24 - thr. It replaced a search over the seven
-// neighbour boundaries with an fp32 threshold (about forty-five VALU
-// operations, partly as branches, against about twenty here): identical
-// over every fp32 magnitude at its threshold and either side of it, and the
-// quantizers ran 22-37% faster with stochastic rounding.
+// randomised). With eb the biased fp32 exponent of a and ec = max(eb, 127),
+// z = a * 2^(128 - ec) is an exact scaling that maps the gap to 1: z lies in
+// [2, 4) for 1 <= a < 6 (gap 2^(eb - 128)), in [1, 2) for 0.5 <= a < 1 and in
+// [0, 1) below (gap 0.5 for both). Then lo has code floor(z) + 2 (ec - 127)
+// and f = z - floor(z), so f * 2^24 is exact, as is the comparison with the
+// integer u24 < 2^24. It replaced a search over the seven neighbour
+// boundaries (about forty-five VALU operations, partly as branches; the
+// quantizers ran 22-37% faster with stochastic rounding); both forms agree
+// on every fp32 magnitude at its threshold and either side of it.
 __device__ __forceinline__ uint32_t e2m1_sr_mag(uint32_t ab, uint32_t u24) {
-  const uint32_t eb = ab >> 23;
-  const uint32_t thr_hi = (ab << (eb >= 127u ? 2 : 1)) & 0xFFFFFFu;
-  const uint32_t thr_lo = (uint32_t)__builtin_ceilf(__fmul_rn(bits_f(ab), 33554432.0f));
-  const uint32_t thr = eb >= 126u ? thr_hi : thr_lo;
-  const uint32_t up = (u24 - thr) >> 31;
-  // both arms computed, then selected (a nested conditional became a branch)
-  const uint32_t base_hi = 2u * eb - 252u + ((ab >> 22) & 1u);
-  const uint32_t base_lo = (uint32_t)(eb == 126u);
-  const uint32_t base = eb >= 127u ? base_hi : base_lo;
-  return ab >= 0x40C00000u ? 7u : base + up;
+  const uint32_t ec = max(ab >> 23, 127u);
+  const float z = __builtin_ldexpf(bits_f(ab), 128 - (int)ec);
+  const uint32_t lo = (uint32_t)z;                           // floor(z), z >= 0
+  const float thr = __fmul_rn(__builtin_amdgcn_fractf(z), 16777216.0f);
+  const uint32_t code = lo + 2u * (ec - 127u) + ((float)u24 < thr ? 1u : 0u);
+  return ab >= 0x40C00000u ? 7u : code;
 }
 
 }  // namespace mx
