@@ -872,8 +872,8 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   const int rb = a.rb > 0 ? a.rb : (RND == MX_K_ROUND_SR ? 2 : 1);
   const int64_t gy = (nkb_pad + rb - 1) / rb;
   // one column per lane, quads sharing Philox: measured 15-18% faster with a
-  // rotation, 2-11% slower without one (there the column-pair kernel stays)
-  if constexpr (RND == MX_K_ROUND_SR && FMT == kFmtE2M1 && ROT != MX_K_ROT_NONE) {
+  // rotation and 21-23% faster without one than the column-pair kernel
+  if constexpr (RND == MX_K_ROUND_SR && FMT == kFmtE2M1) {
     if ((a.cols & 3) == 0)
       return launch(quant_axis0_sr_kernel<ROT>, dim3((unsigned)(mnp / threads), (unsigned)gy),
                     dim3(threads), 0, stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales,

@@ -92,6 +92,25 @@ def test_quantize_every_bf16_pattern(mx, axis, rot, rnd):
 
 
 @pytest.mark.parametrize("rot", ROTS)
+def test_quantize_every_bf16_pattern_axis0_quad_sr(mx, rot):
+    """Every bf16 pattern down the columns of an axis-0 operand whose column
+    count is a multiple of four, the case where stochastic rounding takes the
+    quad-shared Philox kernel (one zero column pads 4163 columns to 4164)."""
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    n_anch = -(-65536 // 31)
+    pad = np.zeros(n_anch * 31, np.uint16)
+    pad[:65536] = allv
+    anch = np.concatenate([np.full((n_anch, 1), 0x40FF, np.uint16), pad.reshape(n_anch, 31)], 1)
+    x = np.concatenate([allv.reshape(2048, 32), anch, np.zeros((1, 32), np.uint16)], 0)
+    x = np.ascontiguousarray(x.T)
+    assert x.shape[1] % 4 == 0
+    q = mx.quantize(to_dev(x), axis=0, rotate=rot, round="sr", seed=0x5EED | (1 << 32))
+    _sync()
+    _check_q(q, oracle.quantize_ref(x, 0, rotate=rot, rounding="sr", seed=0x5EED | (1 << 32)),
+             f"quad sr rot={rot}")
+
+
+@pytest.mark.parametrize("rot", ROTS)
 @pytest.mark.parametrize("rnd", RNDS)
 def test_quantize_special_blocks(mx, rot, rnd):
     f = np.float32
