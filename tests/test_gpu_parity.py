@@ -448,3 +448,78 @@ def test_quantize_axis0_sr_quad_shared_philox(mx, rot, shape, ld):
     _sync()
     _check_q(q, oracle.quantize_ref(x, 0, rotate=rot, rounding="sr", seed=seed),
              f"rot={rot} shape={shape} ld={ld}")
+
+
+# ------------------------------------------------------- size limit
+def _sampled_operand_rows(q, rows):
+    """Codes and scales of the given operand rows, read from the device
+    buffers one 256-row panel at a time (a panel's codes are contiguous in
+    the tiled layout)."""
+    mnp, kp = oracle.padded_extents(q.mn, q.k)
+    panel = 256 * kp // 2
+    scales = oracle.untile_scales(host_u8(q.scales), q.mn, q.k)
+    codes = np.empty((len(rows), q.k), np.uint8)
+    cache = {}
+    for i, m in enumerate(rows):
+        p = int(m) // 256
+        if p not in cache:
+            cache[p] = oracle.untile_codes(host_u8(q.codes[p * panel:(p + 1) * panel]), 256, q.k)
+        codes[i] = cache[p][int(m) % 256]
+    return codes, scales[rows]
+
+
+def _host_bits(t) -> np.ndarray:
+    import torch
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_operands_at_the_size_limit(mx):
+    """A 130816 x 16384 source, whose operands in either orientation hold
+    1 GiB - 2 MiB of codes (the largest the host accepts is just under
+    1 GiB), quantized with random signs and stochastic rounding along both
+    axes; sampled operand rows (the first and the last included) bit-exact
+    against the oracle, then an Fprop over 130816 rows and a Wgrad over a
+    130816-long reduction, sampled output rows within the GEMM bound."""
+    import torch
+    R, C = 130816, 16384
+    mnp, kp = oracle.padded_extents(R, C)
+    assert mnp * kp // 2 == (1 << 30) - (1 << 21)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0x51CE)
+    x = torch.randn((R, C), generator=g, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn((256, C), generator=g, device="cuda", dtype=torch.bfloat16)
+    x2 = torch.randn((R, 64), generator=g, device="cuda", dtype=torch.bfloat16)
+    rot, rnd, s = "rand_sign_hadamard", "sr", 0x3C3C
+    sa, sb = s, s | (1 << 32)
+
+    # Fprop: A = q(x, axis 1) over all 130816 rows, B = q(w, axis 1)
+    qa = mx.quantize(x, 1, rot, rnd, seed=sa)
+    qb = mx.quantize(w, 1, rot, rnd, seed=sb)
+    y = mx.linear("fprop", qa, qb, "f32")
+    _sync()
+    rng = np.random.default_rng(9)
+    ms = np.unique(np.r_[0, R - 1, rng.choice(R, 30, replace=False)])
+    ra = oracle.quantize_ref(_host_bits(x[torch.from_numpy(ms).cuda()]), 1, rotate=rot,
+                             rounding=rnd, seed=sa, row_index=ms, total_cols=C)
+    codes, scales = _sampled_operand_rows(qa, ms)
+    assert np.array_equal(codes, ra.codes) and np.array_equal(scales, ra.scales)
+    rb = oracle.quantize_ref(_host_bits(w), 1, rotate=rot, rounding=rnd, seed=sb)
+    got = y[torch.from_numpy(ms).cuda()].cpu().numpy()
+    err = rel_fro(got, oracle.mx_gemm_ref(ra, rb))
+    assert err <= GEMM_TOL, f"fprop at the limit: rel Frobenius {err:.3e}"
+    del qa, y
+
+    # Wgrad: A = q(x, axis 0) (16384 operand rows, K = 130816), B = q(x2, axis 0)
+    qa0 = mx.quantize(x, 0, rot, rnd, seed=sa)
+    qb0 = mx.quantize(x2, 0, rot, rnd, seed=sb)
+    dw = mx.linear("wgrad", qa0, qb0, "f32")
+    _sync()
+    ns = np.unique(np.r_[0, C - 1, rng.choice(C, 20, replace=False)])
+    ra0 = oracle.quantize_ref(_host_bits(x[:, torch.from_numpy(ns).cuda()]), 0, rotate=rot,
+                              rounding=rnd, seed=sa, col_index=ns, total_cols=C)
+    codes0, scales0 = _sampled_operand_rows(qa0, ns)
+    assert np.array_equal(codes0, ra0.codes) and np.array_equal(scales0, ra0.scales)
+    rb0 = oracle.quantize_ref(_host_bits(x2), 0, rotate=rot, rounding=rnd, seed=sb)
+    got0 = dw[torch.from_numpy(ns).cuda()].cpu().numpy()
+    err0 = rel_fro(got0, oracle.mx_gemm_ref(ra0, rb0))
+    assert err0 <= GEMM_TOL, f"wgrad at the limit: rel Frobenius {err0:.3e}"
