@@ -479,7 +479,9 @@ def test_operands_at_the_size_limit(mx):
     1 GiB), quantized with random signs and stochastic rounding along both
     axes; sampled operand rows (the first and the last included) bit-exact
     against the oracle, then an Fprop over 130816 rows and a Wgrad over a
-    130816-long reduction, sampled output rows within the GEMM bound."""
+    130816-long reduction, sampled output rows within the GEMM bound; the
+    dual quantizer's two outputs equal the two single launches byte for
+    byte."""
     import torch
     R, C = 130816, 16384
     mnp, kp = oracle.padded_extents(R, C)
@@ -507,7 +509,7 @@ def test_operands_at_the_size_limit(mx):
     got = y[torch.from_numpy(ms).cuda()].cpu().numpy()
     err = rel_fro(got, oracle.mx_gemm_ref(ra, rb))
     assert err <= GEMM_TOL, f"fprop at the limit: rel Frobenius {err:.3e}"
-    del qa, y
+    del y
 
     # Wgrad: A = q(x, axis 0) (16384 operand rows, K = 130816), B = q(x2, axis 0)
     qa0 = mx.quantize(x, 0, rot, rnd, seed=sa)
@@ -523,3 +525,10 @@ def test_operands_at_the_size_limit(mx):
     got0 = dw[torch.from_numpy(ns).cuda()].cpu().numpy()
     err0 = rel_fro(got0, oracle.mx_gemm_ref(ra0, rb0))
     assert err0 <= GEMM_TOL, f"wgrad at the limit: rel Frobenius {err0:.3e}"
+    del dw
+
+    # both orientations from one read: byte-identical to the two launches above
+    qd1, qd0 = mx.quantize_dual(x, rot, rnd, seed1=sa, seed0=sa)
+    _sync()
+    for got_q, want_q in ((qd1, qa), (qd0, qa0)):
+        assert torch.equal(got_q.codes, want_q.codes) and torch.equal(got_q.scales, want_q.scales)
