@@ -119,7 +119,6 @@ __all__ = [
     "mx_gemm_ref",
     "linear_ref",
     "bf16_round_ref",
-    "operand_mse",
     "fwht16x2_f32",
     "ROT_HADAMARD16",
     "FMT_FP4",
@@ -666,9 +665,3 @@ def bf16_round_ref(x: np.ndarray) -> np.ndarray:
     nan = np.isnan(x)
     out[nan] = np.uint16(0x7FC0)
     return out
-
-
-def operand_mse(q: QuantRef) -> float:
-    """Mean squared quantization error in the rotated domain (fp64)."""
-    d = dequantize_ref(q.codes, q.scales)
-    return float(np.mean((d - q.rotated.astype(np.float64)) ** 2))
