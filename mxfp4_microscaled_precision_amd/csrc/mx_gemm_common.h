@@ -177,8 +177,13 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&ac
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int r = k * 8 + rr;
-        const uint4 d = *reinterpret_cast<const uint4 *>(slab + r * 128 + ((ch ^ (r & 7)) << 4));
-        *reinterpret_cast<uint4 *>(pi + k * step + h * 128) = d;
+        const v4i d = *reinterpret_cast<const v4i *>(slab + r * 128 + ((ch ^ (r & 7)) << 4));
+        // fp32 tiles (Wgrad) store non-temporally: measured 2-3% faster
+        // there; the bf16 ops measured slower with it and keep plain stores
+        if (OUT_BF16)
+          *reinterpret_cast<v4i *>(pi + k * step + h * 128) = d;
+        else
+          __builtin_nontemporal_store(d, reinterpret_cast<v4i *>(pi + k * step + h * 128));
       }
     }
     pi += 2 * step;
