@@ -72,7 +72,7 @@ typedef enum mx_round {
  * throughput against the FP8 baseline; ShowAPI page
  * "AMD颠覆认知：FP4不稳定性的真正原因", section 2.2: E4M3 as an FP8 format). */
 typedef enum mx_format {
-  MX_FMT_FP4_E2M1 = 0,  /* written by mx_quantize / mx_quantize_dual           */
+  MX_FMT_FP4_E2M1 = 0,  /* written by mx_quantize / _dual / _pair             */
   MX_FMT_FP8_E4M3 = 1   /* written by mx_quantize_fp8                         */
 } mx_format;
 
@@ -196,6 +196,33 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
                            int32_t block, int32_t rotate, int32_t round, uint64_t seed1,
                            uint64_t seed0, void *codes1, void *scales1, void *codes0,
                            void *scales0, mx_qtensor *desc1, mx_qtensor *desc0, void *stream);
+
+/*
+ * Two axis-1 quantizations in one launch: the Fprop pair X [T, in] and
+ * W [out, in], which share their reduction extent (36Kr, section
+ * "Fehlerdiagnoseexperiment": Fprop takes X and W, both quantized along
+ * `in`). One persistent grid walks the row groups of A and then of B, which
+ * saves one launch's ramp and drain.
+ *
+ *   xa_bf16, rows_a, lda / xb_bf16, rows_b, ldb : the two sources
+ *       [rows_a, cols] and [rows_b, cols], each as x_bf16, rows, ld of
+ *       mx_quantize with axis 1 (ld % 8 == 0, 16-byte aligned).
+ *   cols, block, rotate, round : shared; cols % 32 == 0, block == 32.
+ *   seed_a / seed_b : as seed of mx_quantize for each operand (for an Fprop,
+ *       s and s | 1 << 32: shared random signs, independent SR noise).
+ *   codes_a, scales_a, desc_a / codes_b, scales_b, desc_b : as codes,
+ *       scales, out_desc of mx_quantize with axis 1, one set per operand.
+ *   Either operand may be empty (rows 0). Ownership, alignment, the
+ *   descriptors (may be NULL) and the error codes are as for mx_quantize,
+ *   checked for A and then for B before anything is launched. The results
+ *   are byte-identical to the two mx_quantize calls.
+ */
+mx_status mx_quantize_pair(const void *xa_bf16, int64_t rows_a, int64_t lda,
+                           const void *xb_bf16, int64_t rows_b, int64_t ldb, int64_t cols,
+                           int32_t block, int32_t rotate, int32_t round, uint64_t seed_a,
+                           uint64_t seed_b, void *codes_a, void *scales_a, void *codes_b,
+                           void *scales_b, mx_qtensor *desc_a, mx_qtensor *desc_b,
+                           void *stream);
 
 /*
  * Byte sizes of the tiled codes and scales of mx_quantize_fp8 (codes: one

@@ -24,6 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "LIB_PATH", "MxError", "QTensorDesc", "QTensor", "load_library", "library_symbols",
     "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "quantize_dual",
+    "quantize_pair",
     "quantize_fp8_sizes", "quantize_fp8", "linear",
     "ROTATE", "ROUND", "FORMATS", "OPS", "OUT_DTYPES", "OP_AXES",
 ]
@@ -81,6 +82,13 @@ _SIGNATURES = {
                                    ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.POINTER(QTensorDesc), ctypes.c_void_p]),
     "mx_quantize_dual": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.POINTER(QTensorDesc),
+                                        ctypes.POINTER(QTensorDesc), ctypes.c_void_p]),
+    "mx_quantize_pair": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint64,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -251,6 +259,33 @@ def quantize(x, axis: int, rotate: str = "hadamard", round: str = "rne", seed: i
                          ctypes.byref(desc), _stream_handle(x.device, stream))
     _check(st, "mx_quantize")
     return QTensor(codes, scales, desc)
+
+
+def quantize_pair(xa, xb, rotate: str = "hadamard", round: str = "rne", seed_a: int = 0,
+                  seed_b: int = 0, stream=None) -> Tuple[QTensor, QTensor]:
+    """Axis-1 quantizations of two 2-D bf16 CUDA tensors with the same column
+    count in one launch (see mx_quantize_pair): returns (A operand, B operand),
+    byte-identical to quantize(xa, 1, ...) and quantize(xb, 1, ...)."""
+    import torch
+    lib = load_library()
+    ra, cols, lda = _source_extents(xa)
+    rb, cols_b, ldb = _source_extents(xb)
+    if cols != cols_b:
+        raise ValueError("quantize_pair needs sources with the same column count")
+    out = []
+    for rows in (ra, rb):
+        cb, sb = quantize_sizes(rows, cols, 1)
+        out.append((torch.empty((cb,), dtype=torch.uint8, device=xa.device),
+                    torch.empty((sb,), dtype=torch.uint8, device=xa.device)))
+    (ca, sa), (cb_, sb_) = out
+    da, db = QTensorDesc(), QTensorDesc()
+    ptr = lambda t: t.data_ptr() if t.numel() else None  # noqa: E731
+    st = lib.mx_quantize_pair(ptr(xa), ra, lda, ptr(xb), rb, ldb, cols, 32, ROTATE[rotate],
+                              ROUND[round], seed_a & 0xFFFFFFFFFFFFFFFF,
+                              seed_b & 0xFFFFFFFFFFFFFFFF, ptr(ca), ptr(sa), ptr(cb_), ptr(sb_),
+                              ctypes.byref(da), ctypes.byref(db), _stream_handle(xa.device, stream))
+    _check(st, "mx_quantize_pair")
+    return QTensor(ca, sa, da), QTensor(cb_, sb_, db)
 
 
 def quantize_dual(x, rotate: str = "hadamard", round: str = "rne", seed1: int = 0,

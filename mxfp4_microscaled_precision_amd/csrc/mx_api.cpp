@@ -185,6 +185,50 @@ mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_
                       scales, out_desc, stream, MX_FMT_FP8_E4M3);
 }
 
+mx_status mx_quantize_pair(const void *xa_bf16, int64_t rows_a, int64_t lda,
+                           const void *xb_bf16, int64_t rows_b, int64_t ldb, int64_t cols,
+                           int32_t block, int32_t rotate, int32_t round, uint64_t seed_a,
+                           uint64_t seed_b, void *codes_a, void *scales_a, void *codes_b,
+                           void *scales_b, mx_qtensor *desc_a, mx_qtensor *desc_b,
+                           void *stream) {
+  mx_status st = check_quantize(xa_bf16, rows_a, cols, lda, 1, block, rotate, round, codes_a,
+                                scales_a, MX_FMT_FP4_E2M1);
+  if (st != MX_OK) return st;
+  st = check_quantize(xb_bf16, rows_b, cols, ldb, 1, block, rotate, round, codes_b, scales_b,
+                      MX_FMT_FP4_E2M1);
+  if (st != MX_OK) return st;
+  fill_desc(desc_a, codes_a, scales_a, rows_a, cols, 1, block, rotate, round, seed_a,
+            MX_FMT_FP4_E2M1);
+  fill_desc(desc_b, codes_b, scales_b, rows_b, cols, 1, block, rotate, round, seed_b,
+            MX_FMT_FP4_E2M1);
+  const bool live_a = rows_a > 0 && cols > 0, live_b = rows_b > 0 && cols > 0;
+  if (!live_a && !live_b) return MX_OK;
+  mx::QuantArgs q[2];
+  const void *xs[2] = {xa_bf16, xb_bf16};
+  const int64_t rs[2] = {rows_a, rows_b}, lds[2] = {lda, ldb};
+  const uint64_t seeds[2] = {seed_a, seed_b};
+  void *cs[2] = {codes_a, codes_b}, *ss[2] = {scales_a, scales_b};
+  for (int i = 0; i < 2; ++i) {
+    q[i].x = static_cast<const uint16_t *>(xs[i]);
+    q[i].rows = rs[i];
+    q[i].cols = cols;
+    q[i].ld = lds[i];
+    q[i].axis = 1;
+    q[i].rotate = rotate;
+    q[i].round = round;
+    q[i].seed_lo = (uint32_t)(seeds[i] & 0xFFFFFFFFull);
+    q[i].seed_hi = (uint32_t)(seeds[i] >> 32);
+    q[i].codes = static_cast<uint8_t *>(cs[i]);
+    q[i].scales = static_cast<uint8_t *>(ss[i]);
+    q[i].rb = 0;
+    q[i].fmt = 0;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!live_b) return hip_status(mx::quantize_launch(q[0], s));
+  if (!live_a) return hip_status(mx::quantize_launch(q[1], s));
+  return hip_status(mx::quantize_pair_launch(q[0], q[1], s));
+}
+
 mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
                            int32_t block, int32_t rotate, int32_t round, uint64_t seed1,
                            uint64_t seed0, void *codes1, void *scales1, void *codes0,

@@ -43,6 +43,10 @@ struct QuantArgs {
 
 hipError_t quantize_launch(const QuantArgs &a, hipStream_t stream);
 
+// Two axis-1 MXFP4 quantizations of sources with the same column count (and
+// the same rotation and rounding) in one launch.
+hipError_t quantize_pair_launch(const QuantArgs &a, const QuantArgs &b, hipStream_t stream);
+
 // Both orientations of one source (rows % 32 == 0, cols % 32 == 0).
 struct DualArgs {
   const uint16_t *x;   // bf16 [rows, cols], leading dimension ld

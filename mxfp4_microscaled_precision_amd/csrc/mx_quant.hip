@@ -364,17 +364,30 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 // ---------------------------------------------------------------------------
 constexpr int kAxis1WgPerCu = 3;   // 12 waves per compute unit (measured best of 2, 3, 4, 6, 8)
 
-template <int ROT, int RND, int FMT>
+// The second operand of a two-operand launch (PAIR): a source with the same
+// column count whose row groups follow the first operand's in one sequence
+// of tiles, so both are walked by one persistent grid.
+struct Axis1Second {
+  const uint16_t *x;
+  int64_t rows, ld;
+  uint8_t *codes, *scales;
+  uint32_t seed_lo, seed_hi;
+};
+
+template <int ROT, int RND, int FMT, bool PAIR>
 __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
-    uint32_t seed_hi) {
+    uint32_t seed_hi, Axis1Second sec) {
+  static_assert(!PAIR || FMT == kFmtE2M1, "two-operand launches are MXFP4 only");
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][4096];
   __shared__ __attribute__((aligned(16))) uint8_t signs_lds[ROT == MX_K_ROT_RAND_SIGN ? 4 : 1][128];
   const int64_t mnp = (rows + 255) & ~(int64_t)255;
+  const int64_t mnp2 = PAIR ? (sec.rows + 255) & ~(int64_t)255 : 0;
+  const uint32_t gsplit = (uint32_t)(mnp >> 4);   // row groups of the first operand
   // Tile counts fit 32 bits: the host refuses operands of 1 GiB of codes.
   const uint32_t nslices = (uint32_t)((cols + 127) >> 7);
-  const uint32_t ntiles = (uint32_t)(mnp >> 4) * nslices;
+  const uint32_t ntiles = (gsplit + (uint32_t)(mnp2 >> 4)) * nslices;
   const int wv = threadIdx.x >> 6;
   const uint32_t stride = gridDim.x * 4u;
   uint32_t tile = blockIdx.x * 4u + (uint32_t)wv;
@@ -397,13 +410,17 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
   // staging loads of a tile: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
   u32x4 v[4];
   auto load_tile = [&](uint32_t tg, uint32_t tq) {
+    const bool two = PAIR && tg >= gsplit;                  // the tile is the second operand's
+    const uint16_t *xs = two ? sec.x : x;
+    const int64_t rs = two ? sec.rows : rows, ls = two ? sec.ld : ld;
+    const uint32_t lg = two ? tg - gsplit : tg;
     const int64_t k = (int64_t)tq * 128 + ch * 8;           // first element of the chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
-      const int64_t r = (int64_t)tg * 16 + rr;
-      v[j] = (r < rows && k < cols)
-                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + r * ld + k))
+      const int64_t r = (int64_t)lg * 16 + rr;
+      v[j] = (r < rs && k < cols)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xs + r * ls + k))
                  : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -422,9 +439,12 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     if (tile + stride < ntiles) load_tile(gn, qn);          // next tile's loads in flight
 
     const int rr = lane & 15, cb = lane >> 4;
-    const int64_t r = (int64_t)g * 16 + rr;
+    const bool two = PAIR && g >= gsplit;                   // wave-uniform
+    const uint32_t gl = two ? g - gsplit : g;
+    const uint32_t s_lo = two ? sec.seed_lo : seed_lo, s_hi = two ? sec.seed_hi : seed_hi;
+    const int64_t r = (int64_t)gl * 16 + rr;
     const int64_t kb = (int64_t)q * 4 + cb;
-    const bool valid = r < rows && (kb << 5) < cols;
+    const bool valid = r < (two ? sec.rows : rows) && (kb << 5) < cols;
     float y[32];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -440,7 +460,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
       // make one each, the sign bits meet in LDS as one nibble per call
       uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
       if (lane < 32) {
-        const U4 sw = sign_words((uint32_t)(q * 32 + lane), seed_lo);
+        const U4 sw = sign_words((uint32_t)(q * 32 + lane), s_lo);
         sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
       }
       __builtin_amdgcn_wave_barrier();
@@ -457,7 +477,7 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
     const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
     U4 w{0u, 0u, 0u, 0u};
     auto u24_of = [&](int i) -> uint32_t {
-      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), seed_lo, seed_hi);
+      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), s_lo, s_hi);
       return pick_word(w, (uint32_t)(i & 3)) >> 8;
     };
     constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
@@ -473,10 +493,11 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
       *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
       *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
     } else {
-      *reinterpret_cast<uint4 *>(codes + (size_t)tile * 1024 + lane * 16) =
+      const uint32_t lt = PAIR ? gl * nslices + q : tile;   // tile within its operand
+      *reinterpret_cast<uint4 *>((two ? sec.codes : codes) + (size_t)lt * 1024 + lane * 16) =
           make_uint4(out[0], out[1], out[2], out[3]);
     }
-    scales[scale_offset(r, kb, mnp)] = (uint8_t)s;
+    (two ? sec.scales : scales)[scale_offset(r, kb, two ? mnp2 : mnp)] = (uint8_t)s;
     g = gn;
     q = qn;
     advance(gn, qn);
@@ -861,8 +882,9 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
     const int64_t mnp = (a.rows + 255) & ~(int64_t)255;
     const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
     const int64_t blocks = std::min<int64_t>((ntiles + 3) / 4, (int64_t)cu_count() * kAxis1WgPerCu);
-    return launch(quant_axis1_kernel<ROT, RND, FMT>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                  a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi);
+    return launch(quant_axis1_kernel<ROT, RND, FMT, false>, dim3((unsigned)blocks), dim3(256), 0,
+                  stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi,
+                  Axis1Second{});
   }
   const int threads = 256;
   const int64_t mnp = (a.cols + 255) & ~(int64_t)255;
@@ -886,7 +908,37 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
                 pair_loads);
 }
 
+// Two axis-1 MXFP4 operands with the same column count in one launch: the
+// grid walks the first operand's row groups and then the second's, saving
+// one launch's ramp and drain.
+template <int ROT, int RND>
+hipError_t launch_pair(const QuantArgs &a, const QuantArgs &b, hipStream_t stream) {
+  const int64_t mnp = (a.rows + 255) & ~(int64_t)255, mnp2 = (b.rows + 255) & ~(int64_t)255;
+  const int64_t ntiles = ((mnp + mnp2) >> 4) * ((a.cols + 127) >> 7);
+  const int64_t blocks = std::min<int64_t>((ntiles + 3) / 4, (int64_t)cu_count() * kAxis1WgPerCu);
+  const Axis1Second sec{b.x, b.rows, b.ld, b.codes, b.scales, b.seed_lo, b.seed_hi};
+  return launch(quant_axis1_kernel<ROT, RND, kFmtE2M1, true>, dim3((unsigned)blocks), dim3(256), 0,
+                stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi, sec);
+}
+
 }  // namespace
+
+hipError_t quantize_pair_launch(const QuantArgs &a, const QuantArgs &b, hipStream_t stream) {
+  if (a.axis != 1 || b.axis != 1 || a.fmt != 0 || b.fmt != 0 || a.cols != b.cols ||
+      a.rotate != b.rotate || a.round != b.round)
+    return hipErrorInvalidValue;
+  switch (a.rotate * 2 + a.round) {
+    case 0: return launch_pair<0, 0>(a, b, stream);
+    case 1: return launch_pair<0, 1>(a, b, stream);
+    case 2: return launch_pair<1, 0>(a, b, stream);
+    case 3: return launch_pair<1, 1>(a, b, stream);
+    case 4: return launch_pair<2, 0>(a, b, stream);
+    case 5: return launch_pair<2, 1>(a, b, stream);
+    case 6: return launch_pair<3, 0>(a, b, stream);
+    case 7: return launch_pair<3, 1>(a, b, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t quantize_dual_launch(const DualArgs &a, hipStream_t stream) {
   switch (a.rotate * 2 + a.round) {

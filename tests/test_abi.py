@@ -126,6 +126,38 @@ def test_quantize_rejects_before_launch():
     assert _q(lib, P, -1, 64, 64) == -2
 
 
+def _qp(lib, xa, ra, lda, xb, rb, ldb, cols, block=32, rot=1, rnd=0, ca=16, sa=16, cb=4096,
+        sb=4096, da=None, db=None):
+    return lib.mx_quantize_pair(xa, ra, lda, xb, rb, ldb, cols, block, rot, rnd, 5, 6, ca, sa,
+                                cb, sb, da, db, None)
+
+
+def test_quantize_pair_rejects_before_launch():
+    """Both operands are validated as mx_quantize would, A first, before any HIP call."""
+    lib = mx.load_library()
+    P = 4096
+    assert _qp(lib, P, 64, 64, P, 64, 64, 64, block=16) == -4
+    assert _qp(lib, P, 64, 64, P, 64, 64, 64, rot=7) == -4
+    assert _qp(lib, P, 64, 64, P, 64, 64, 48) == -2            # K % 32
+    assert _qp(lib, P, 64, 32, P, 64, 64, 64) == -2            # lda < cols
+    assert _qp(lib, P, 64, 64, P, 64, 32, 64) == -2            # ldb < cols
+    assert _qp(lib, P + 2, 64, 64, P, 64, 64, 64) == -3        # A misaligned
+    assert _qp(lib, P, 64, 64, P + 2, 64, 64, 64) == -3        # B misaligned
+    assert _qp(lib, P, 64, 64, P, 64, 68, 64) == -3            # ldb % 8
+    assert _qp(lib, P, 64, 64, None, 64, 64, 64) == -1
+    assert _qp(lib, P, 64, 64, P, 64, 64, 64, cb=None) == -1
+    assert _qp(lib, P, 64, 1 << 14, P, 1 << 17, 1 << 14, 1 << 14) == -6   # B codes of 1 GiB
+
+
+def test_quantize_pair_empty_fills_both_descriptors():
+    lib = mx.load_library()
+    da, db = mx.QTensorDesc(), mx.QTensorDesc()
+    assert _qp(lib, None, 0, 64, None, 0, 64, 64, rot=2, rnd=1, ca=None, sa=None, cb=None,
+               sb=None, da=ctypes.byref(da), db=ctypes.byref(db)) == 0
+    assert (da.rows, da.cols, da.axis, da.rotate, da.round, da.seed) == (0, 64, 1, 2, 1, 5)
+    assert (db.rows, db.cols, db.axis, db.rotate, db.round, db.seed) == (0, 64, 1, 2, 1, 6)
+
+
 def test_quantize_empty_is_a_noop_and_fills_descriptor():
     lib = mx.load_library()
     desc = mx.QTensorDesc()

@@ -532,3 +532,38 @@ def test_operands_at_the_size_limit(mx):
     _sync()
     for got_q, want_q in ((qd1, qa), (qd0, qa0)):
         assert torch.equal(got_q.codes, want_q.codes) and torch.equal(got_q.scales, want_q.scales)
+
+
+# ------------------------------------------------------- two-operand launch
+@pytest.mark.parametrize("ra,rb,cols", [(37, 300, 160), (1000, 256, 512), (0, 64, 96),
+                                        (64, 0, 96), (20000, 5000, 608)])
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_pair_matches_two_launches(mx, ra, rb, cols, rot, rnd):
+    """One launch over two axis-1 operands that share their column count
+    (the Fprop pair X, W): both outputs byte-identical to the two single
+    launches, ragged row counts, an empty side, and 7920 tiles walked by
+    3072 waves across the boundary between the operands."""
+    rng = np.random.default_rng(ra * 7 + rb + cols)
+    xa, xb = to_dev(_rand_bits(rng, (ra, cols))), to_dev(_rand_bits(rng, (rb, cols)))
+    sa, sb = 0x77, 0x77 | (1 << 32)
+    pa, pb = mx.quantize_pair(xa, xb, rot, rnd, seed_a=sa, seed_b=sb)
+    qa = mx.quantize(xa, 1, rot, rnd, seed=sa)
+    qb = mx.quantize(xb, 1, rot, rnd, seed=sb)
+    _sync()
+    for p, q in ((pa, qa), (pb, qb)):
+        assert np.array_equal(host_u8(p.codes), host_u8(q.codes))
+        assert np.array_equal(host_u8(p.scales), host_u8(q.scales))
+
+
+def test_quantize_pair_strided_against_oracle(mx):
+    """Row-strided sources of different strides, random signs and SR, each
+    output against the oracle directly."""
+    rng = np.random.default_rng(31)
+    a, b = _rand_bits(rng, (300, 224), 2.0), _rand_bits(rng, (77, 224), 0.5)
+    ta, tb = to_dev_strided(a, ld=240), to_dev_strided(b, ld=256)
+    sa, sb = 0x1D, 0x1D | (1 << 32)
+    pa, pb = mx.quantize_pair(ta, tb, "rand_sign_hadamard", "sr", seed_a=sa, seed_b=sb)
+    _sync()
+    _check_q(pa, oracle.quantize_ref(a, 1, rotate="rand_sign_hadamard", rounding="sr", seed=sa), "A")
+    _check_q(pb, oracle.quantize_ref(b, 1, rotate="rand_sign_hadamard", rounding="sr", seed=sb), "B")
