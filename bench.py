@@ -698,7 +698,15 @@ def bench_block(mx, wls, steps):
             d["ms"] += m["ms_per_step"]
             lin = wl.name[len("block_"):].rsplit("_", 1)[0]
             if lin in SHARED_INPUT_LINEARS and wl.op in ("fprop", "wgrad"):
-                d["saved_ms"] += 1e-3 * (m["t_quant_a_us"] if wl.op == "fprop" else m["t_quant_b_us"])
+                if wl.op == "wgrad":
+                    saved = 1e-3 * m["t_quant_b_us"]
+                elif rr.pcalls is not None:
+                    # X and W in one launch: what X adds is the step less W's own
+                    # launch and the GEMM
+                    saved = max(0.0, m["ms_per_step"] - 1e-3 * (m["t_quant_b_us"] + m["t_gemm_us"]))
+                else:
+                    saved = 1e-3 * m["t_quant_a_us"]
+                d["saved_ms"] += saved
             d["ops"][wl.name] = {"ms": round(m["ms_per_step"], 4), "tflops": round(m["tflops"], 1),
                                  "t_gemm_us": round(m["t_gemm_us"], 1)}
             del rr
