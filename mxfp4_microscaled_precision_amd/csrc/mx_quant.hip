@@ -292,18 +292,6 @@ __device__ __forceinline__ void quantize_pair_sr(const float (&va)[32], const fl
   }
 }
 
-__device__ __forceinline__ void apply_signs(float (&y)[32], uint32_t k0, uint32_t seed_lo) {
-  // k0 is a multiple of 32: indices k0 + i, counters (k0 >> 2) + i / 4
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const U4 s = sign_words((k0 >> 2) + q, seed_lo);
-    y[4 * q + 0] = bits_f(f_bits(y[4 * q + 0]) ^ (s.x & 0x80000000u));
-    y[4 * q + 1] = bits_f(f_bits(y[4 * q + 1]) ^ (s.y & 0x80000000u));
-    y[4 * q + 2] = bits_f(f_bits(y[4 * q + 2]) ^ (s.z & 0x80000000u));
-    y[4 * q + 3] = bits_f(f_bits(y[4 * q + 3]) ^ (s.w & 0x80000000u));
-  }
-}
-
 // Sign bits of K indices 4 ctr .. 4 ctr + 3 as a nibble (bit j for index
 // 4 ctr + j), from one Philox call of the sign stream.
 __device__ __forceinline__ uint32_t sign_nibble(uint32_t ctr, uint32_t seed_lo) {
@@ -538,6 +526,12 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
 #pragma unroll
     for (int j = 0; j < kWords; ++j) oa[j] = ob[j] = 0u;
     uint32_t sa = 0u, sb = 0u;                     // padding: zero codes, scale code 0
+    // random signs: the block's 32 rows need the 8 sign calls at counters
+    // 8 kb + j, the same for every column; lane j makes call j and the bits
+    // are gathered with readlane, before any lane of the wave branches off
+    uint32_t smask = 0u;
+    if (ROT == MX_K_ROT_RAND_SIGN)
+      smask = gather_sign_mask(sign_nibble((uint32_t)((kb << 3) + (threadIdx.x & 7)), seed_lo), 0);
     if (kb < nkb && has_a) {
       float ya[32], yb[32];
       const uint16_t *src = x + (kb << 5) * ld + c0;
@@ -563,8 +557,8 @@ __global__ __launch_bounds__(256) void quant_axis0_kernel(
         }
       }
       if (ROT == MX_K_ROT_RAND_SIGN) {
-        apply_signs(ya, (uint32_t)(kb << 5), seed_lo);
-        apply_signs(yb, (uint32_t)(kb << 5), seed_lo);
+        apply_sign_mask(ya, smask);
+        apply_sign_mask(yb, smask);
       }
       rotate_block<ROT>(ya);
       rotate_block<ROT>(yb);
