@@ -1,18 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of the MXFP4 linear-layer hot path on one MI355X.
 
-One step = rotate + quantize operand A, rotate + quantize operand B, MXFP4 GEMM
-(fp32 accumulation), i.e. the whole hot path of one GEMM of the triple, with
-the inputs already resident in HBM. The headline workload is the Fprop of a
-Llama-3.1-8B q_proj layer: X 8192x4096 bf16 (0.1% of channels x50), W
-4096x4096 bf16, 32-point Hadamard + RNE along K = 4096, bf16 output.
+Headline workload (default, --workload block): the 21 GEMMs of one
+Llama-3.1-8B transformer block at 16384 tokens -- q/k/v/o (4096x4096,
+1024x4096 twice, 4096x4096), gate/up (14336x4096) and down (4096x14336),
+each as Fprop Y = X W^T, Dgrad dX = dY W and Wgrad dW = dY^T X -- with every
+operand rotated by the 32-point Hadamard and quantized to MXFP4 (E8M0 scale
+per 32 elements, E2M1 elements, round to nearest even).
+
+One step is one training step's linear-layer work of the block, with the
+inputs already resident in HBM: for each linear, X, W and dY are each
+quantized once into both packed orientations (mx_quantize_dual), then Fprop
+(bf16 out), Dgrad (bf16 out) and Wgrad (fp32 out) run on those operands.
+`value` is the 21 GEMMs' 2*M*N*K over the step time, i.e. TFLOP/s including
+the Hadamard and the quantization. The block's working set (about 8 GB)
+exceeds the 256 MB last-level cache many times over, so every step reads
+its inputs from HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
-                    [--all] [--no-cpu-baseline]
+                    [--all] [--structural] [--no-cpu-baseline]
 
-Prints ONE JSON line. `value` is TFLOP/s including the two quantizations
-(2*M*N*K / step time). The inputs are replicated so that consecutive steps
-read different copies and the working set exceeds the last-level cache.
+Prints ONE JSON line. --workload fprop_q_proj (or wgrad_gate_proj,
+dgrad_down_proj) times one GEMM of the triple with its two quantizations as
+the step instead.
 """
 from __future__ import annotations
 
@@ -36,45 +46,347 @@ LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 CSRC = "mxfp4_microscaled_precision_amd/csrc/"
 GEMM_SRC = (CSRC + "mx_gemm.hip", CSRC + "mx_gemm_common.h")
 GEMM_E4M3_SRC = (CSRC + "mx_gemm_e4m3.hip", CSRC + "mx_gemm_common.h")
-WORKLOADS_REF = None
+QUANT_SRC = (CSRC + "mx_quant.hip", CSRC + "mx_device.h")
 GEMM_TRAFFIC = "profiles/gemm_{}_traffic.md"
 GEMM_E4M3_TRAFFIC = "profiles/gemm_e4m3_{}_traffic.md"
-QUANT_SRC = (CSRC + "mx_quant.hip", CSRC + "mx_device.h")
 QUANT_TRAFFIC = "profiles/quant_{}_traffic.md"
 QUANT_E4M3_TRAFFIC = "profiles/quant_e4m3_{}_traffic.md"
+BLOCK_GEMM_TRAFFIC = "profiles/gemm_bf16_block_t16384_traffic.md"
+BLOCK_QUANT_TRAFFIC = "profiles/quant_dual_block_t16384_traffic.md"
+SETTLE_MS = 40.0   # sustained load before timing: the clock settles in about this long
+WORKLOADS_REF = None
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    # about 40 ms of back-to-back steps: the clock settles under sustained load
-    # (measured: 10 warmup steps time the step ~15% slow, 400 and more agree)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--workload", default="fprop_q_proj")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps after the settle phase (at least 40 ms of steps "
+                         "back to back always runs first)")
+    ap.add_argument("--workload", default="block")
     ap.add_argument("--variant", default=None)
+    ap.add_argument("--tokens", type=int, default=16384, help="block workload: tokens T")
     ap.add_argument("--format", default="fp4_e2m1", choices=("fp4_e2m1", "fp8_e4m3"),
-                    help="element format of the timed path (fp8_e4m3: the MXFP8 comparator)")
+                    help="element format of a single-GEMM workload (fp8_e4m3: the MXFP8 "
+                         "comparator)")
     ap.add_argument("--all", action="store_true",
-                    help="also time every other workload/variant and the full block")
+                    help="also time every single-GEMM workload and variant, the block with "
+                         "per-op quantization, the dual quantizer and the quantization error")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="block workload: skip the q_proj Fprop and FP8-comparator figures")
     ap.add_argument("--structural", action="store_true",
                     help="also run the repeated-Wgrad structural-error harness")
-    ap.add_argument("--cpu-reps", type=int, default=3,
-                    help="repetitions of the whole-workload oracle run (cpu_baseline)")
+    ap.add_argument("--cpu-reps", type=int, default=1,
+                    help="repetitions of the oracle run (cpu_baseline)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB three "
                          "times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
+def _dev_bf16(bits, device="cuda"):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).to(device)
+
+
+# ------------------------------------------------------------------ timing
+def settle(fn, min_ms=SETTLE_MS):
+    """Run fn(i) back to back for at least min_ms of GPU time (untimed,
+    sized from a short first burst); returns the number of calls."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(3):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1) / 3, 1e-3)
+    n = int(math.ceil(min_ms / per))
+    for i in range(n):
+        fn(3 + i)
+    torch.cuda.synchronize()
+    return 3 + n
+
+
+def timed(fn, steps, warmup=0):
+    """Average ms per call of fn(i): at least SETTLE_MS of calls back to back,
+    then `warmup` more, then `steps` calls between one pair of HIP events on
+    the current stream (the stream the library launches on), bracketed by
+    device synchronisation. Returns (ms per call, wall ms per call)."""
+    import torch
+    settle(fn)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+# ------------------------------------------------------ the Llama block
+class BlockRunner:
+    """The 7 linears of one Llama-3.1-8B block at T tokens, resident on the
+    GPU with their quantized operands and outputs; pre-marshalled C-ABI
+    calls (no torch calls inside a step)."""
+
+    def __init__(self, mx, tokens=16384, keep_host=("k_proj",)):
+        import torch
+        from datagen import LLAMA_BLOCK_LINEARS, block_workloads, workload_tensors
+        self.mx = mx
+        self.lib = mx.load_library()
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.T = tokens
+        wls = block_workloads(tokens)
+        self.variants = wls[0].variants
+        self.lins = []
+        self.host = {}
+        for li, lin in enumerate(LLAMA_BLOCK_LINEARS):
+            wl = [w for w in wls if w.data_seed == 500 + li and w.op == "fprop"][0]
+            t = workload_tensors(wl)
+            if lin.name in keep_host:
+                self.host[lin.name] = t
+            src = {k: _dev_bf16(t[k]) for k in ("X", "W", "dY")}
+            del t
+            bufs = {}
+            for k, x in src.items():
+                rows, cols = x.shape
+                for axis in (1, 0):
+                    cb, sb = mx.quantize_sizes(rows, cols, axis)
+                    bufs[k, axis] = (torch.empty(cb, dtype=torch.uint8, device="cuda"),
+                                     torch.empty(sb, dtype=torch.uint8, device="cuda"),
+                                     mx.QTensorDesc())
+            T, o, i = tokens, lin.out_features, lin.in_features
+            outs = {"fprop": torch.empty((T, o), dtype=torch.bfloat16, device="cuda"),
+                    "dgrad": torch.empty((T, i), dtype=torch.bfloat16, device="cuda"),
+                    "wgrad": torch.empty((o, i), dtype=torch.float32, device="cuda")}
+            self.lins.append({"name": lin.name, "out": o, "in": i, "src": src, "bufs": bufs,
+                              "outs": outs})
+            print(f"[bench] block {lin.name}: {T}x{i} -> {o} resident", file=sys.stderr,
+                  flush=True)
+        torch.cuda.synchronize()
+        self.calls = []
+
+    # (A, B) of each op as (tensor, axis), and the output dtype
+    OPS = (("fprop", ("X", 1), ("W", 1), "bf16"), ("dgrad", ("dY", 1), ("W", 0), "bf16"),
+           ("wgrad", ("dY", 0), ("X", 0), "f32"))
+
+    def flops(self):
+        return sum(3 * 2.0 * self.T * L["out"] * L["in"] for L in self.lins)
+
+    def _seeds(self, seed):
+        """Seeds by role: X is A of Fprop (axis 1) and B of Wgrad (axis 0);
+        W is B of Fprop and of Dgrad; dY is A of Dgrad and of Wgrad."""
+        sa = seed & 0xFFFFFFFF
+        sb = sa | (1 << 32)
+        return {"X": (sa, sb), "W": (sb, sb), "dY": (sa, sa)}
+
+    def build(self, label, per_op=False):
+        """The launch list of one step of variant `label`: a list of
+        (kind, info, fn, args). With per_op, each op quantizes its own two
+        operands (Fprop's pair in one launch) right before its GEMM."""
+        mx, lib, st = self.mx, self.lib, self.stream
+        _, rot, rnd, seed = [v for v in self.variants if v[0] == label][0]
+        R, D = mx.ROTATE[rot], mx.ROUND[rnd]
+        seeds = self._seeds(seed)
+        calls = []
+        for L in self.lins:
+            src, bufs = L["src"], L["bufs"]
+
+            def qargs(k, axis):
+                x = src[k]
+                c, s, d = bufs[k, axis]
+                sd = seeds[k][0] if axis == 1 else seeds[k][1]
+                return (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), axis, 32, R, D, sd,
+                        c.data_ptr(), s.data_ptr(), ctypes.byref(d), st)
+
+            def gemm(op, a, b, odt):
+                C = L["outs"][op]
+                m, n = C.shape
+                k = self.T if op == "wgrad" else (L["in"] if op == "fprop" else L["out"])
+                return ("gemm_" + odt, {"linear": L["name"], "op": op, "M": m, "N": n, "K": k},
+                        lib.mx_linear, (mx.OPS[op], ctypes.byref(bufs[a][2]),
+                                        ctypes.byref(bufs[b][2]), C.data_ptr(), C.stride(0),
+                                        mx.OUT_DTYPES[odt], st))
+
+            if not per_op:
+                for k in ("X", "W", "dY"):
+                    x = src[k]
+                    c1, s1, d1 = bufs[k, 1]
+                    c0, s0, d0 = bufs[k, 0]
+                    calls.append(("quant_dual", {"linear": L["name"], "tensor": k,
+                                                 "elems": x.numel()}, lib.mx_quantize_dual,
+                                  (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), 32, R, D,
+                                   seeds[k][0], seeds[k][1], c1.data_ptr(), s1.data_ptr(),
+                                   c0.data_ptr(), s0.data_ptr(), ctypes.byref(d1),
+                                   ctypes.byref(d0), st)))
+                for op, a, b, odt in self.OPS:
+                    calls.append(gemm(op, a, b, odt))
+            else:
+                for op, a, b, odt in self.OPS:
+                    if op == "fprop":
+                        x, w = src["X"], src["W"]
+                        cx, sx, dx = bufs["X", 1]
+                        cw, sw, dw = bufs["W", 1]
+                        calls.append(("quant_pair", {"linear": L["name"], "elems": x.numel() + w.numel()},
+                                      lib.mx_quantize_pair,
+                                      (x.data_ptr(), x.shape[0], x.stride(0), w.data_ptr(),
+                                       w.shape[0], w.stride(0), x.shape[1], 32, R, D,
+                                       seeds["X"][0], seeds["W"][0], cx.data_ptr(),
+                                       sx.data_ptr(), cw.data_ptr(), sw.data_ptr(),
+                                       ctypes.byref(dx), ctypes.byref(dw), st)))
+                    else:
+                        for k, axis in (a, b):
+                            calls.append(("quant_single", {"linear": L["name"], "tensor": k,
+                                                           "axis": axis,
+                                                           "elems": src[k].numel()},
+                                          lib.mx_quantize, qargs(k, axis)))
+                    calls.append(gemm(op, a, b, odt))
+        self.calls = calls
+        return calls
+
+    def step(self, i=0):
+        for kind, _, fn, args in self.calls:
+            if fn(*args):
+                raise RuntimeError(f"library call {fn.__name__} failed")
+
+    def instrumented(self, steps):
+        """`steps` steps with a HIP event before every launch and after the
+        last: per-launch durations (ms), summed over the steps, in launch
+        order, and the instrumented ms per step."""
+        import torch
+        n = len(self.calls)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        tot = [0.0] * n
+        step_ms = 0.0
+        for s in range(steps):
+            for j, (kind, _, fn, args) in enumerate(self.calls):
+                ev[j].record()
+                if fn(*args):
+                    raise RuntimeError("library call failed")
+            ev[n].record()
+            torch.cuda.synchronize()
+            for j in range(n):
+                tot[j] += ev[j].elapsed_time(ev[j + 1])
+            step_ms += ev[0].elapsed_time(ev[n])
+        return [t / steps for t in tot], step_ms / steps
+
+
+def gemm_bytes(M, N, K, out_bytes, code_bytes=0.5):
+    return (M + N) * K * (code_bytes + 1.0 / 32) + M * N * out_bytes
+
+
+def block_bench(mx, args):
+    """The headline: the block under every variant (dual quantizer), the
+    det. Hadamard one instrumented per launch."""
+    br = BlockRunner(mx, args.tokens)
+    flops = br.flops()
+    labels = [v[0] for v in br.variants]
+    head = args.variant or labels[0]
+    res = {}
+    for label in [head] + [lb for lb in labels if lb != head]:
+        br.build(label)
+        ms, wall = timed(br.step, args.steps, args.warmup)
+        res[label] = {"ms_per_step": ms, "wall_ms_per_step": wall,
+                      "tflops": flops / (ms * 1e-3) / 1e12}
+        print(f"[bench] block {label}: {ms:.3f} ms/step, {res[label]['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+    # per-launch split of the headline variant
+    calls = br.build(head)
+    settle(br.step)
+    per_launch, inst_ms = br.instrumented(args.steps)
+    split = {}
+    per_op = {}
+    for (kind, info, _, _), ms in zip(calls, per_launch):
+        d = split.setdefault(kind, {"us": 0.0, "launches": 0, "flops": 0.0, "bytes": 0.0})
+        d["us"] += ms * 1e3
+        d["launches"] += 1
+        if kind.startswith("gemm"):
+            f = 2.0 * info["M"] * info["N"] * info["K"]
+            d["flops"] += f
+            d["bytes"] += gemm_bytes(info["M"], info["N"], info["K"], 2 if kind == "gemm_bf16" else 4)
+            per_op[f"{info['linear']}/{info['op']}"] = {
+                "M": info["M"], "N": info["N"], "K": info["K"], "us": round(ms * 1e3, 2),
+                "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        else:
+            d["bytes"] += info["elems"] * (2 + 2 * (0.5 + 1.0 / 32))
+    return br, res, head, split, per_op, inst_ms
+
+
+def cpu_baseline_block(br, seed, reps):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    block: the k_proj linear's whole training-step work (X 16384x4096,
+    W 1024x4096, dY 16384x1024 each quantized along both axes with the
+    det. Hadamard, then the three fp64 GEMMs of the dequantized operands),
+    `reps` times; the value is that sample's flops over its mean time."""
+    import oracle
+    t = br.host["k_proj"]
+    X, W, dY = t["X"], t["W"], t["dY"]
+    sa = seed & 0xFFFFFFFF
+    sb = sa | (1 << 32)
+    T, n_in = X.shape
+    n_out = W.shape[0]
+    flops = 3 * 2.0 * T * n_in * n_out
+    t_q = t_g = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        q = {("X", 1): oracle.quantize_ref(X, 1, seed=sa), ("X", 0): oracle.quantize_ref(X, 0, seed=sb),
+             ("W", 1): oracle.quantize_ref(W, 1, seed=sb), ("W", 0): oracle.quantize_ref(W, 0, seed=sb),
+             ("dY", 1): oracle.quantize_ref(dY, 1, seed=sa),
+             ("dY", 0): oracle.quantize_ref(dY, 0, seed=sa)}
+        t1 = time.perf_counter()
+        oracle.mx_gemm_ref(q["X", 1], q["W", 1])
+        oracle.mx_gemm_ref(q["dY", 1], q["W", 0])
+        oracle.mx_gemm_ref(q["dY", 0], q["X", 0])
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        t_g += t2 - t1
+        del q
+    per = (t_q + t_g) / reps
+    return {
+        "value": round(flops / per / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": _blas_threads() or len(os.sched_getaffinity(0)),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "quantizer_threads": 1,
+        "kind": "oracle",
+        "sample": (f"k_proj linear of the block (T={T}, in={n_in}, out={n_out}), det. Hadamard: "
+                   f"oracle quantization of X, W, dY along both axes (NumPy, 1 thread, "
+                   f"{t_q / reps:.2f} s) + the three fp64 GEMMs of the dequantized operands "
+                   f"(BLAS, {t_g / reps:.2f} s), x{reps}; {flops / 1e9:.1f} GFLOP of the "
+                   f"block's {br.flops() / 1e9:.1f}"),
+        "sample_seconds": round(t_q + t_g, 2),
+    }
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return None
+
+
+# --------------------------------------------------- one GEMM of the triple
 class Runner:
-    """Pre-marshalled C-ABI calls for one workload variant (no torch calls in
-    the timed loop)."""
+    """Pre-marshalled C-ABI calls for one single-GEMM workload variant (no
+    torch calls in the timed loop). The inputs are replicated so that
+    consecutive steps read different copies (min_bytes of sources)."""
 
     def __init__(self, mx, w, variant, tensors=None, min_bytes=2 * LLC_BYTES, device="cuda",
                  fmt="fp4_e2m1"):
-        import numpy as np
         import torch
         from datagen import operands_for, workload_tensors
 
@@ -92,12 +404,7 @@ class Runner:
         self.ncopy = max(1, math.ceil(min_bytes / per_copy))
         lib = mx.load_library()
         self.lib = lib
-
-        def dev(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
-                torch.bfloat16).to(device)
-
-        a0, b0 = dev(a_src), dev(b_src)
+        a0, b0 = _dev_bf16(a_src, device), _dev_bf16(b_src, device)
         self.A = [a0] + [a0.clone() for _ in range(self.ncopy - 1)]
         self.B = [b0] + [b0.clone() for _ in range(self.ncopy - 1)]
         stream = torch.cuda.current_stream().cuda_stream
@@ -165,7 +472,6 @@ class Runner:
         if self.lib.mx_linear(*self.lcalls[i % self.ncopy]):
             raise RuntimeError("mx_linear failed")
 
-    # algorithmic work
     def flops(self):
         return 2.0 * self.M * self.N * self.K
 
@@ -173,84 +479,27 @@ class Runner:
         return 1.0 if self.fmt == "fp8_e4m3" else 0.5
 
     def quant_bytes(self, shape):
-        n = shape[0] * shape[1]
-        return n * (2 + self.code_bytes() + 1.0 / 32)
+        return shape[0] * shape[1] * (2 + self.code_bytes() + 1.0 / 32)
 
     def gemm_bytes(self):
         ob = 4 if self.out_dtype == "f32" else 2
-        return (self.M + self.N) * self.K * (self.code_bytes() + 1.0 / 32) + self.M * self.N * ob
+        return gemm_bytes(self.M, self.N, self.K, ob, self.code_bytes())
 
 
-SETTLE_MS = 40.0   # sustained load before timing: the clock settles in about this long
-
-
-def settle(fn, min_ms=SETTLE_MS):
-    """Run fn(i) back to back for at least min_ms of GPU time (untimed
-    warmup sized from a short first burst); returns the number of calls."""
-    import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(5):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    per = max(e0.elapsed_time(e1) / 5, 1e-3)
-    n = int(math.ceil(min_ms / per))
-    for i in range(n):
-        fn(5 + i)
-    torch.cuda.synchronize()
-    return 5 + n
-
-
-def time_loop(fn, iters, warmup=None):
-    """Average ms per call of fn(i) over `iters` back-to-back calls, between
-    one pair of HIP events on the current stream (the stream the library
-    launches on)."""
-    import torch
-    if warmup is None:
-        settle(fn)
-    for i in range(warmup or 0):
-        fn(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(iters):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
-
-
-def measure(r, steps, warmup=None):
+def measure(r, steps, warmup=0):
     """The timed region: `steps` whole steps (quantize A, quantize B, GEMM)
-    back to back, after `warmup` untimed steps (None: as many as SETTLE_MS of
-    load takes). Then each kernel alone, back to back, for its average
-    launch duration (events between the kernels of a step would add gaps)."""
-    import torch
-    if warmup is None:
-        settle(r.step)
-    for i in range(warmup or 0):
-        r.step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(steps):
-        r.step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / steps
-    t_qa = time_loop(r.quant_a, max(steps, 10), 3)
-    t_qb = time_loop(r.quant_b, max(steps, 10), 3)
-    t_g = time_loop(r.gemm, max(steps, 10), 3)
+    back to back after the settle phase and `warmup` more steps. Then each
+    kernel alone, settled and back to back, for its average launch
+    duration (events between the kernels of a step would add gaps)."""
+    ms, wall = timed(r.step, steps, warmup)
+    n = max(steps, 10)
+    t_qa = timed(r.quant_a, n)[0]
+    t_qb = timed(r.quant_b, n)[0]
+    t_g = timed(r.gemm, n)[0]
     flops = r.flops()
     return {
         "ms_per_step": ms,
-        "wall_ms_per_step": wall * 1e3 / steps,
+        "wall_ms_per_step": wall,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "t_quant_a_us": t_qa * 1e3,
         "t_quant_b_us": t_qb * 1e3,
@@ -262,18 +511,11 @@ def measure(r, steps, warmup=None):
 
 
 def cpu_baseline(r, reps):
-    """The oracle as it stands, on the host cores: the whole workload
-    (quantize both operands, fp64 GEMM of the dequantized operands), `reps`
-    times; the value is the workload's flops over the mean time."""
-    import numpy as np  # noqa: F401
-
+    """The oracle as it stands, on the host cores: the whole single-GEMM
+    workload (quantize both operands, fp64 GEMM of the dequantized
+    operands), `reps` times; the value is the workload's flops over the mean
+    time."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                            if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas_threads = None
     seed_a = r.seed & 0xFFFFFFFF
     t_q = t_g = 0.0
     for _ in range(reps):
@@ -292,7 +534,7 @@ def cpu_baseline(r, reps):
     return {
         "value": round(r.flops() / per / 1e12, 5),
         "unit": "TFLOP/s",
-        "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+        "cores": _blas_threads() or len(os.sched_getaffinity(0)),
         "affinity_cores": len(os.sched_getaffinity(0)),
         "quantizer_threads": 1,
         "kind": "oracle",
@@ -328,26 +570,9 @@ def recorded_traffic(kernel_src, summary):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
-                                   "(sharding across GPUs is not implemented)"}))
-        sys.exit(2)
-    import torch
-
-    import mxfp4_microscaled_precision_amd as mx
-    from datagen import WORKLOADS, block_workloads, workload_tensors
-    global WORKLOADS_REF
-    WORKLOADS_REF = WORKLOADS
-
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    mx.load_library()
-    w = WORKLOADS[args.workload]
-    variant = args.variant or w.variants[0][0]
-    print(f"[bench] workload {w.name} variant {variant}", file=sys.stderr, flush=True)
+def single_workload_line(mx, args, w, variant):
+    """The bench line of a single-GEMM workload (--workload other than
+    block)."""
     fp8 = args.format == "fp8_e4m3"
     r = Runner(mx, w, variant, fmt=args.format)
     res = measure(r, args.steps, args.warmup)
@@ -357,6 +582,7 @@ def main():
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_FP4_TFLOPS
     gemm_src, gemm_prof = (GEMM_E4M3_SRC, GEMM_E4M3_TRAFFIC) if fp8 else (GEMM_SRC, GEMM_TRAFFIC)
     quant_prof = QUANT_E4M3_TRAFFIC if fp8 else QUANT_TRAFFIC
+    elem = "fp8_e4m3" if fp8 else "fp4_e2m1"
     out = {
         "metric": METRIC,
         "value": round(res["tflops"], 2),
@@ -368,8 +594,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3xfp8_e4m3->f32" if fp8 else "fp4_e2m1xfp4_e2m1->f32",
-        "data": "synthetic (seeded PCG64; Llama-3.1-8B q_proj shapes, no real weights)",
+        "dtype": elem,
+        "out_dtype": w.out_dtype,
+        "data": "synthetic (seeded PCG64; Llama-3.1-8B layer shapes, no real weights or data)",
         "config": {
             "workload": (f"{w.name}: {w.op} M={r.M} N={r.N} K={r.K}, rotate={r.rot}, "
                          f"round={r.rnd}, out={w.out_dtype}"),
@@ -395,40 +622,157 @@ def main():
             "frac": round(qa_ach / PEAK_HBM_GBS, 4),
             "traffic": recorded_traffic(QUANT_SRC, quant_prof.format(w.name)),
         },
-        "per_kernel_us": {k: round(res[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
-                                                       "t_gemm_us")},
+        "per_kernel_us_alone": {k: round(res[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
+                                                             "t_gemm_us")},
         "quant_b_gbs": round(res["quant_b_gbs"], 1),
         "gemm_only_tflops": round(res["gemm_tflops"], 2),
     }
-    if not fp8 and r.rnd == "rne":
-        out["fp8_comparator"] = fp8_comparator(mx, w, variant, max(10, args.steps // 4), res)
-        print(f"[bench] fp8 comparator {out['fp8_comparator']}", file=sys.stderr, flush=True)
+    return r, res, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
+        sys.exit(2)
+    import torch
+
+    import mxfp4_microscaled_precision_amd as mx
+    from datagen import WORKLOADS, workload_tensors
+    global WORKLOADS_REF
+    WORKLOADS_REF = WORKLOADS
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    mx.load_library()
+    print(f"[bench] workload {args.workload}", file=sys.stderr, flush=True)
+
+    if args.workload == "block":
+        br, res, head, split, per_op, inst_ms = block_bench(mx, args)
+        h = res[head]
+        flops = br.flops()
+        dom = split["gemm_bf16"]
+        dom_ach = dom["flops"] / (dom["us"] * 1e-6) / 1e12
+        q = split["quant_dual"]
+        q_ach = q["bytes"] / (q["us"] * 1e-6) / 1e9
+        g_all_us = split["gemm_bf16"]["us"] + split["gemm_f32"]["us"]
+        g_all_fl = split["gemm_bf16"]["flops"] + split["gemm_f32"]["flops"]
+        out = {
+            "metric": METRIC,
+            "value": round(h["tflops"], 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(h["ms_per_step"], 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "fp4_e2m1",
+            "out_dtype": "bf16 (Fprop, Dgrad), f32 (Wgrad); fp32 accumulation",
+            "data": ("synthetic (seeded PCG64, chunked streams; Llama-3.1-8B block shapes, "
+                     "no real weights or data)"),
+            "config": {
+                "workload": (f"Llama-3.1-8B block T={br.T}: 7 linears x Fprop/Dgrad/Wgrad "
+                             f"(21 MXFP4 GEMMs), {head}, each of X/W/dY quantized once "
+                             f"into both orientations"),
+                "tokens": br.T, "variant": head, "gemms": 21,
+                "gflop_per_step": round(flops / 1e9, 1),
+                "launches_per_step": len(br.calls),
+            },
+            "pct_mfma_peak": round(100.0 * h["tflops"] / PEAK_FP4_TFLOPS, 2),
+            "roofline": {
+                "kernel": "gemm_tiled_kernel<1, 0> (MXFP4 GEMM, bf16 out: the 14 Fprop and "
+                          "Dgrad GEMMs of a step)",
+                "bound": "mfma",
+                "achieved": round(dom_ach, 2),
+                "peak": PEAK_FP4_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(dom_ach / PEAK_FP4_TFLOPS, 4),
+                "traffic": recorded_traffic(GEMM_SRC, BLOCK_GEMM_TRAFFIC),
+                "launches": dom["launches"],
+                "avg_gflop_per_launch": round(dom["flops"] / dom["launches"] / 1e9, 3),
+                "avg_us_per_launch": round(dom["us"] / dom["launches"], 2),
+                "algorithmic_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
+            },
+            "quant_roofline": {
+                "kernel": "quant_dual_kernel (both orientations from one read)",
+                "bound": "hbm",
+                "achieved": round(q_ach, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(q_ach / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic(QUANT_SRC, BLOCK_QUANT_TRAFFIC),
+                "avg_us_per_launch": round(q["us"] / q["launches"], 2),
+                "algorithmic_bytes_per_launch": round(q["bytes"] / q["launches"]),
+            },
+            "gemm_all": {"tflops": round(g_all_fl / (g_all_us * 1e-6) / 1e12, 2),
+                         "frac": round(g_all_fl / (g_all_us * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4)},
+            "per_kernel_us": {k: round(v["us"], 1) for k, v in split.items()},
+            "instrumented_ms_per_step": round(inst_ms, 5),
+            "per_op": per_op,
+            "variants": {lb: {"ms_per_step": round(v["ms_per_step"], 5),
+                              "tflops": round(v["tflops"], 2),
+                              "pct_mfma_peak": round(100 * v["tflops"] / PEAK_FP4_TFLOPS, 2)}
+                         for lb, v in res.items()},
+        }
+        if args.all:
+            per = {}
+            for label in [v[0] for v in br.variants]:
+                br.build(label, per_op=True)
+                ms, _ = timed(br.step, args.steps, args.warmup)
+                per[label] = {"ms_per_step": round(ms, 5),
+                              "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+                print(f"[bench] block per-op {label}: {ms:.3f} ms", file=sys.stderr, flush=True)
+            out["per_op_quantization"] = per
+        if not args.no_secondary:
+            w = WORKLOADS["fprop_q_proj"]
+            r, sres, _ = single_workload_line(mx, args, w, "det_hadamard")
+            out["secondary"] = {"fprop_q_proj": {
+                "tflops": round(sres["tflops"], 2), "ms_per_step": round(sres["ms_per_step"], 5),
+                "gemm_us_alone": round(sres["t_gemm_us"], 2),
+                "gemm_frac": round(sres["gemm_tflops"] / PEAK_FP4_TFLOPS, 4),
+                "quant_a_gbs": round(sres["quant_a_gbs"], 1)}}
+            out["secondary"]["fp8_comparator"] = fp8_comparator(mx, w, "det_hadamard",
+                                                                max(10, args.steps), sres)
+            del r
+            wg = WORKLOADS["wgrad_gate_proj"]
+            out["secondary"]["wgrad_gate_proj_quant_error"] = quant_error(
+                mx, wg, [v[0] for v in wg.variants])
+            print(f"[bench] quant error {out['secondary']['wgrad_gate_proj_quant_error']}",
+                  file=sys.stderr, flush=True)
+        if args.all:
+            add_all(mx, args, out, skip=None)
+        if args.structural or args.all:
+            out["structural_error"] = structural_error(mx)
+            print("[bench] structural error done", file=sys.stderr, flush=True)
+        copy_calibration(args, out)
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = cpu_baseline_block(br, 0, args.cpu_reps)
+        print(json.dumps(out), flush=True)
+        return
+
+    w = WORKLOADS[args.workload]
+    variant = args.variant or w.variants[0][0]
+    r, res, out = single_workload_line(mx, args, w, variant)
+    if args.format != "fp8_e4m3" and r.rnd == "rne":
+        out["fp8_comparator"] = fp8_comparator(mx, w, variant, max(10, args.steps), res)
     if args.all:
-        extra = {}
-        for name, wl in WORKLOADS.items():
-            if name == "tiny_wgrad":
-                continue
-            t = workload_tensors(wl)
-            for v in wl.variants:
-                if name == w.name and v[0] == variant:
-                    continue
-                rr = Runner(mx, wl, v[0], tensors=t)
-                m = measure(rr, max(10, args.steps // 4))
-                extra[f"{name}/{v[0]}"] = {k: round(val, 3) for k, val in m.items()}
-                print(f"[bench] {name}/{v[0]}: {m['tflops']:.1f} TFLOP/s", file=sys.stderr,
-                      flush=True)
-                del rr
-        out["other_workloads"] = extra
-        out["dual_quantizer"] = dual_quant_bench(mx, max(10, args.steps // 2))
-        print(f"[bench] dual quantizer {out['dual_quantizer']}", file=sys.stderr, flush=True)
-        wg = WORKLOADS["wgrad_gate_proj"]
-        out["wgrad_gate_proj_quant_error"] = output_mse(mx, wg, [v[0] for v in wg.variants])
-        print(f"[bench] quant error {out['wgrad_gate_proj_quant_error']}", file=sys.stderr,
-              flush=True)
-        out["block"] = bench_block(mx, block_workloads(), max(5, args.steps // 20))
+        add_all(mx, args, out, skip=(w.name, variant))
     if args.structural or args.all:
         out["structural_error"] = structural_error(mx)
-        print("[bench] structural error done", file=sys.stderr, flush=True)
+    copy_calibration(args, out)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(r, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
+def copy_calibration(args, out):
+    import torch
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -437,10 +781,32 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(r, args.cpu_reps)
-    print(json.dumps(out), flush=True)
+
+
+def add_all(mx, args, out, skip):
+    """--all: every single-GEMM workload and variant, the dual quantizer
+    alone, and the quantization error of the Wgrad gate/up workload."""
+    from datagen import WORKLOADS, workload_tensors
+    extra = {}
+    for name, wl in WORKLOADS.items():
+        if name == "tiny_wgrad":
+            continue
+        t = workload_tensors(wl)
+        for v in wl.variants:
+            if skip is not None and (name, v[0]) == skip:
+                continue
+            rr = Runner(mx, wl, v[0], tensors=t)
+            m = measure(rr, max(10, args.steps))
+            extra[f"{name}/{v[0]}"] = {k: round(val, 3) for k, val in m.items()}
+            print(f"[bench] {name}/{v[0]}: {m['tflops']:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+            del rr
+    out["other_workloads"] = extra
+    out["dual_quantizer"] = dual_quant_bench(mx, max(10, args.steps))
+    print(f"[bench] dual quantizer {out['dual_quantizer']}", file=sys.stderr, flush=True)
+    if "secondary" not in out:
+        wg = WORKLOADS["wgrad_gate_proj"]
+        out["wgrad_gate_proj_quant_error"] = quant_error(mx, wg, [v[0] for v in wg.variants])
 
 
 def fp8_comparator(mx, w, variant, steps, fp4_res):
@@ -455,8 +821,8 @@ def fp8_comparator(mx, w, variant, steps, fp4_res):
     out = {
         "ms_per_step": round(m8["ms_per_step"], 5),
         "tflops": round(m8["tflops"], 2),
-        "per_kernel_us": {k: round(m8[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
-                                                      "t_gemm_us")},
+        "per_kernel_us_alone": {k: round(m8[k], 2) for k in ("t_quant_a_us", "t_quant_b_us",
+                                                            "t_gemm_us")},
         "gemm_tflops": round(fl / (m8["t_gemm_us"] * 1e-6) / 1e12, 2),
         "gemm_frac_fp8_peak": round(fl / (m8["t_gemm_us"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
         "quant_a_gbs": round(m8["quant_a_gbs"], 1),
@@ -467,10 +833,19 @@ def fp8_comparator(mx, w, variant, steps, fp4_res):
     return out
 
 
-def output_mse(mx, wl, variants):
-    """Quantization error at the output of one GEMM: the fp32 MXFP4 result
-    against the fp32 product of the unquantized bf16 operands (torch.matmul on
-    the GPU), as mean squared error and relative Frobenius error."""
+def quant_error(mx, wl, variants):
+    """Quantization error of one GEMM's operands and output (the Wgrad
+    gate/up workload, rotation off and on).
+
+    Operand level: mean((deq - y)^2) over each operand, where deq is the
+    library's dequantization (mx_dequantize) of the quantized operand and y
+    the rotated source, y = R x with R the same block rotation applied in
+    fp32 by a torch matmul with the 32 x 32 matrix (measurement only; R is
+    orthonormal, so this equals the error in the source's own domain up to
+    fp32 rounding).
+    Output level: the fp32 MXFP4 result against the fp32 product of the
+    unquantized bf16 operands (torch.matmul), as mean squared error and
+    relative Frobenius error."""
     import torch
     from datagen import operands_for, workload_tensors
     t = workload_tensors(wl)
@@ -490,11 +865,42 @@ def output_mse(mx, wl, variants):
         b = b if ax_b == 1 else b.t().contiguous()        # [N, K]
         ref = torch.matmul(a, b.t().contiguous())
         d = (c - ref).double()
-        res[label] = {"output_mse": float((d * d).mean()),
-                      "rel_fro": float(d.norm() / ref.double().norm())}
-        del rr, a, b, ref, d, c
+        entry = {"output_mse": float((d * d).mean()),
+                 "rel_fro": float(d.norm() / ref.double().norm())}
+        del d, ref, c
+        for name, q, xs, ax in (("A", rr.qa[0], rr.A[0], ax_a), ("B", rr.qb[0], rr.B[0], ax_b)):
+            deq = mx.dequantize(q)                          # the source's shape, fp32
+            x = xs.float()
+            if ax == 0:                                     # reduction along the rows
+                deq, x = deq.t().contiguous(), x.t().contiguous()
+            y = rotate_rows(x, rr.rot)                      # [MN, K], rotated along K
+            e = (deq - y).double()
+            entry[f"operand_{name}_mse"] = float((e * e).mean())
+            entry[f"operand_{name}_rel_fro"] = float(e.norm() / y.double().norm())
+            del deq, x, y, e
+        res[label] = entry
+        del rr, a, b
         torch.cuda.empty_cache()
     return res
+
+
+def rotate_rows(x, rot):
+    """y = x with every 32-element block of each row multiplied by the
+    rotation R = H / sqrt(32) (H the Sylvester Hadamard matrix), in fp32 on
+    the GPU with torch (measurement only); rot 'none' returns x."""
+    import torch
+    if rot == "none":
+        return x
+    if rot != "hadamard":
+        raise ValueError(rot)
+    i = torch.arange(32, device=x.device)
+    pc = torch.zeros((32, 32), dtype=torch.int64, device=x.device)
+    v = i[:, None] & i[None, :]
+    for b in range(5):
+        pc += (v >> b) & 1
+    H = torch.where(pc % 2 == 0, 1.0, -1.0).to(torch.float32) / math.sqrt(32.0)
+    m, k = x.shape
+    return torch.matmul(x.reshape(m * (k // 32), 32), H.t().contiguous()).reshape(m, k)
 
 
 def dual_quant_bench(mx, steps):
@@ -506,7 +912,7 @@ def dual_quant_bench(mx, steps):
     res = {}
     for wname, tname in (("fprop_q_proj", "X"), ("wgrad_gate_proj", "dY")):
         src = workload_tensors(WORKLOADS_REF[wname])[tname]
-        x = torch.from_numpy(src.view("int16")).view(torch.bfloat16).to("cuda")
+        x = _dev_bf16(src)
         copies = [x] + [x.clone() for _ in range(max(0, (512 << 20) // (2 * x.numel())))]
         lib = mx.load_library()
         st = torch.cuda.current_stream().cuda_stream
@@ -535,9 +941,9 @@ def dual_quant_bench(mx, steps):
                     raise RuntimeError("mx_quantize failed")
             return f
 
-        t_d = time_loop(dual, steps) * 1e3
-        t_1 = time_loop(single(1), steps) * 1e3
-        t_0 = time_loop(single(0), steps) * 1e3
+        t_d = timed(dual, steps)[0] * 1e3
+        t_1 = timed(single(1), steps)[0] * 1e3
+        t_0 = timed(single(0), steps)[0] * 1e3
         n = rows * cols
         res[f"{wname}/{tname} {rows}x{cols}"] = {
             "dual_us": round(t_d, 2), "axis1_us": round(t_1, 2), "axis0_us": round(t_0, 2),
@@ -555,174 +961,76 @@ STRUCTURAL_VARIANTS = (("det_hadamard", "hadamard", "rne", False),
                        ("hadamard_sr", "hadamard", "sr", True))
 
 
-def structural_error(mx, T=8192, n_out=2048, n_in=1024, steps=64, data_seed=3):
-    """Error of Wgrad repeated over `steps` steps on fixed tensors.
-
-    dY [T, n_out] = 1e-4 t_3 and X [T, n_in] ~ N(0, 1) (bf16, the Wgrad
-    gate/up distributions) stay fixed; step k computes dW_k = dY^T X through
-    the MXFP4 path (both operands quantized along T), with seed k for the
-    randomized variants (random signs, stochastic rounding) and the same
-    deterministic rotation every step otherwise. For K = 1, 2, 4, ... the
-    relative Frobenius error of the K-step mean against the fp32 product of
-    the bf16 operands is reported, with the single-step error: a fixed error
-    pattern keeps the mean's error at the single-step value, a pattern that
-    changes from step to step lets it fall. The reference product is a plain
-    torch fp32 matmul (measurement only)."""
+def structural_inputs(T, n_out, n_in, data_seed=3):
+    """The harness's fixed tensors (bf16 bits): dY [T, n_out] = 1e-4 t_3 and
+    X [T, n_in] ~ N(0, 1), the Wgrad gate/up distributions."""
     import numpy as np
-    import torch
     from datagen import normal_bf16, student_t_bf16
     rng = np.random.Generator(np.random.PCG64(data_seed))
     dY = student_t_bf16(rng, (T, n_out), 3.0, 1e-4)
     X = normal_bf16(rng, (T, n_in), 1.0)
-    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to("cuda")  # noqa: E731
-    dYd, Xd = dev(dY), dev(X)
-    ref = torch.matmul(dYd.float().t().contiguous(), Xd.float())
-    ref_norm = ref.double().norm().item()
+    return dY, X
+
+
+def structural_step_seed(k, reseed):
+    """Seed of step k (1-based): k for the randomized variants, 0 otherwise;
+    operand A (dY) takes it, operand B (X) takes it | 1 << 32."""
+    return k if reseed else 0
+
+
+def structural_error(mx, T=8192, n_out=2048, n_in=1024, steps=64, data_seed=3, keep_steps=0):
+    """Error of Wgrad repeated over `steps` steps on fixed tensors.
+
+    dY and X (structural_inputs) stay fixed; step k computes
+    dW_k = dY^T X through the MXFP4 path (both operands quantized along T),
+    with seed k for the randomized variants (random signs, stochastic
+    rounding) and the same deterministic rotation every step otherwise. For
+    K = 1, 2, 4, ... the relative Frobenius error of the K-step mean against
+    the exact product of the bf16 operands is reported, with the single-step
+    error: a fixed error pattern keeps the mean's error at the single-step
+    value, a pattern that changes from step to step lets it fall. The
+    reference product is formed in fp64 on the host from the bf16 values
+    (exact up to fp64 summation). keep_steps > 0 also returns, under
+    "_steps", the first keep_steps steps' quantized operands and dW (host
+    copies) of every variant."""
+    import numpy as np
+    import torch
+    dY, X = structural_inputs(T, n_out, n_in, data_seed)
+    dYd, Xd = _dev_bf16(dY), _dev_bf16(X)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    ref = f(dY).T @ f(X)
+    ref_norm = float(np.linalg.norm(ref))
+    ref_d = torch.from_numpy(ref).to("cuda")
     out = {"shape": {"T": T, "out": n_out, "in": n_in}, "steps": steps, "variants": {}}
+    kept = {}
     Ks = [k for k in (1, 2, 4, 8, 16, 32, 64, 128, 256) if k <= steps]
     for label, rot, rnd, reseed in STRUCTURAL_VARIANTS:
-        acc = torch.zeros_like(ref, dtype=torch.float64)
+        acc = torch.zeros_like(ref_d)
         single = []
         curve = {}
         for k in range(1, steps + 1):
-            seed = k if reseed else 0
+            seed = structural_step_seed(k, reseed)
             qa = mx.quantize(dYd, 0, rot, rnd, seed=seed)
             qb = mx.quantize(Xd, 0, rot, rnd, seed=seed | (1 << 32))
             c = mx.linear("wgrad", qa, qb, "f32")
             acc += c.double()
+            if k <= keep_steps:
+                kept.setdefault(label, []).append({
+                    "seed": seed, "a_codes": qa.codes.cpu().numpy(),
+                    "a_scales": qa.scales.cpu().numpy(), "b_codes": qb.codes.cpu().numpy(),
+                    "b_scales": qb.scales.cpu().numpy(), "dW": c.cpu().numpy()})
             if k <= 4:
-                single.append(((c.double() - ref.double()).norm() / ref_norm).item())
+                single.append(((c.double() - ref_d).norm() / ref_norm).item())
             if k in Ks:
-                curve[k] = ((acc / k - ref.double()).norm() / ref_norm).item()
+                curve[k] = ((acc / k - ref_d).norm() / ref_norm).item()
         out["variants"][label] = {
             "rotate": rot, "round": rnd, "new_seed_per_step": reseed,
             "single_step_rel_err": [round(v, 6) for v in single],
             "mean_rel_err": {str(k): round(v, 6) for k, v in curve.items()},
             "mean_over_single": round(curve[Ks[-1]] / single[0], 4)}
+    if keep_steps:
+        out["_steps"] = kept
     return out
-
-
-# Linears whose input X a real block shares with an earlier one (q/k/v read
-# the same normed hidden state, gate/up the same one): their X quantizations
-# (Fprop operand A, axis 1; Wgrad operand B, axis 0) could be reused.
-SHARED_INPUT_LINEARS = ("k_proj", "v_proj", "up_proj")
-
-
-def block_dual_linear(mx, wl, tensors, steps):
-    """One linear of the block as a training step runs it with the dual-output
-    quantizer: X, W and dY are each quantized once into both orientations
-    (mx_quantize_dual), then Fprop, Dgrad and Wgrad run on those operands.
-    The operands are byte for byte those of the per-op quantizations. Returns
-    {variant: ms per linear}."""
-    import numpy as np
-    import torch
-    lib = mx.load_library()
-    st = torch.cuda.current_stream().cuda_stream
-
-    def dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
-            torch.bfloat16).to("cuda")
-
-    src = {k: dev(tensors[k]) for k in ("X", "W", "dY")}
-    T, n_out, n_in = wl.tokens, wl.out_features, wl.in_features
-    bufs, descs = {}, {}
-    for k, x in src.items():
-        rows, cols = x.shape
-        for axis in (1, 0):
-            cb, sb = mx.quantize_sizes(rows, cols, axis)
-            bufs[k, axis] = (torch.empty(cb, dtype=torch.uint8, device="cuda"),
-                             torch.empty(sb, dtype=torch.uint8, device="cuda"))
-            descs[k, axis] = mx.QTensorDesc()
-    outs = {"fprop": torch.empty((T, n_out), dtype=torch.bfloat16, device="cuda"),
-            "dgrad": torch.empty((T, n_in), dtype=torch.bfloat16, device="cuda"),
-            "wgrad": torch.empty((n_out, n_in), dtype=torch.float32, device="cuda")}
-    # (A, B) of each op, as (tensor, axis)
-    ops = {"fprop": (("X", 1), ("W", 1)), "dgrad": (("dY", 1), ("W", 0)),
-           "wgrad": (("dY", 0), ("X", 0))}
-    res = {}
-    for label, rot, rnd, seed in wl.variants:
-        sa = seed & 0xFFFFFFFF
-        sb_ = sa | (1 << 32)
-        # seeds by role: X is A of Fprop and B of Wgrad; W is B of both of
-        # its ops; dY is A of both of its ops
-        seeds = {"X": (sa, sb_), "W": (sb_, sb_), "dY": (sa, sa)}
-
-        def step(i):
-            for k, x in src.items():
-                s1, s0 = seeds[k]
-                if lib.mx_quantize_dual(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), 32,
-                                        mx.ROTATE[rot], mx.ROUND[rnd], s1, s0,
-                                        bufs[k, 1][0].data_ptr(), bufs[k, 1][1].data_ptr(),
-                                        bufs[k, 0][0].data_ptr(), bufs[k, 0][1].data_ptr(),
-                                        ctypes.byref(descs[k, 1]), ctypes.byref(descs[k, 0]), st):
-                    raise RuntimeError("mx_quantize_dual failed")
-            for op, (a, b) in ops.items():
-                c = outs[op]
-                if lib.mx_linear(mx.OPS[op], ctypes.byref(descs[a]), ctypes.byref(descs[b]),
-                                 c.data_ptr(), c.stride(0), 1 if op != "wgrad" else 0, st):
-                    raise RuntimeError("mx_linear failed")
-
-        res[label] = time_loop(step, steps)
-    del src, bufs, outs
-    torch.cuda.empty_cache()
-    return res
-
-
-def bench_block(mx, wls, steps):
-    """Full Llama-3.1-8B block: 7 linears x {fprop, dgrad, wgrad} per variant.
-
-    Each op quantizes its own two operands (the primary figure). The
-    `shared_input` figure also drops the X quantizations that k/v reuse from
-    q and up from gate, using the same measured per-kernel times. The
-    `dual_quantizer` figure times each linear as a training step runs it:
-    X, W and dY quantized once each into both orientations, then the three
-    GEMMs (block_dual_linear)."""
-    import torch
-    from datagen import workload_tensors
-    res = {}
-    cache = {}
-    dual_ms = {}
-    for wl in wls:
-        key = wl.data_seed
-        if key not in cache:
-            cache.clear()
-            torch.cuda.empty_cache()
-            cache[key] = workload_tensors(wl)
-            for v, ms in block_dual_linear(mx, wl, cache[key], steps).items():
-                dual_ms[v] = dual_ms.get(v, 0.0) + ms
-        for v in wl.variants:
-            rr = Runner(mx, wl, v[0], tensors=cache[key], min_bytes=0)
-            m = measure(rr, steps)
-            d = res.setdefault(v[0], {"flops": 0.0, "ms": 0.0, "saved_ms": 0.0, "ops": {}})
-            d["flops"] += rr.flops()
-            d["ms"] += m["ms_per_step"]
-            lin = wl.name[len("block_"):].rsplit("_", 1)[0]
-            if lin in SHARED_INPUT_LINEARS and wl.op in ("fprop", "wgrad"):
-                if wl.op == "wgrad":
-                    saved = 1e-3 * m["t_quant_b_us"]
-                elif rr.pcalls is not None:
-                    # X and W in one launch: what X adds is the step less W's own
-                    # launch and the GEMM
-                    saved = max(0.0, m["ms_per_step"] - 1e-3 * (m["t_quant_b_us"] + m["t_gemm_us"]))
-                else:
-                    saved = 1e-3 * m["t_quant_a_us"]
-                d["saved_ms"] += saved
-            d["ops"][wl.name] = {"ms": round(m["ms_per_step"], 4), "tflops": round(m["tflops"], 1),
-                                 "t_gemm_us": round(m["t_gemm_us"], 1)}
-            del rr
-        print(f"[bench] block {wl.name} done", file=sys.stderr, flush=True)
-    for v, d in res.items():
-        d["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 2)
-        d["pct_mfma_peak"] = round(100 * d["tflops"] / PEAK_FP4_TFLOPS, 2)
-        ms_shared = d["ms"] - d.pop("saved_ms")
-        d["shared_input"] = {"ms": round(ms_shared, 4),
-                             "tflops": round(d["flops"] / (ms_shared * 1e-3) / 1e12, 2)}
-        if v in dual_ms:
-            d["dual_quantizer"] = {"ms": round(dual_ms[v], 4),
-                                   "tflops": round(d["flops"] / (dual_ms[v] * 1e-3) / 1e12, 2),
-                                   "pct_mfma_peak": round(100 * d["flops"] / (dual_ms[v] * 1e-3)
-                                                          / 1e12 / PEAK_FP4_TFLOPS, 2)}
-    return res
 
 
 if __name__ == "__main__":

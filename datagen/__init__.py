@@ -8,20 +8,30 @@ Erkenntnis ...", section "Fehlerdiagnoseexperiment": Llama 3.1-8B, MLPerf C4).
 C4 and Llama weights are not available; these tensors stand in for them.
 
 Recipe (every tensor):
-  * draw fp32 values from numpy.random.Generator(PCG64(seed)) in the order the
-    workload lists them, then round each value to bfloat16 with
-    round-to-nearest-even on the fp32 bit pattern;
+  * draw fp32 values from numpy.random.Generator(PCG64(...)), then round each
+    value to bfloat16 with round-to-nearest-even on the fp32 bit pattern;
   * activations X ~ N(0, 1), optionally with round(0.001 * cols) outlier
     channels (columns chosen without replacement) multiplied by 50 before the
     bfloat16 rounding;
   * weights W ~ N(0, 0.02^2);
   * output gradients dY = 1e-4 * Student-t(nu = 3).
 
+Streams. The tiny Wgrad workload draws its tensors in the listed order from
+one PCG64(data_seed) stream. The larger workloads (up to 1.5e9 elements for
+the Llama block at 16384 tokens; one stream would take minutes on one core)
+draw each tensor in chunks of CHUNK_ROWS rows: chunk j of the tensor listed
+t-th comes from PCG64(SeedSequence([data_seed, t, j])) (the outlier columns
+of an activation from PCG64(SeedSequence([data_seed, t, OUTLIER_STREAM]))),
+and the chunks are drawn on a thread pool. The values depend only on the
+seeds, not on the thread count.
+
 Arrays are returned as numpy uint16 bfloat16 bit patterns, row-major.
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Tuple
 
 import numpy as np
@@ -41,15 +51,24 @@ __all__ = [
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bfloat16 (nearest, ties to even); NaN stays NaN."""
+    """Round fp32 values to bfloat16 (nearest, ties to even); NaN stays NaN
+    (sign and payload kept, quiet bit set).
+
+    For every non-NaN pattern u (at most 0xFF800000), u + 0x7FFF + bit 16 of
+    u stays below 2^32, so the sum is formed in uint32 in place.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(x)
+    u = x.reshape(-1).view(np.uint32)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                                   # wraps for NaN patterns only
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
+    nan = np.isnan(x.reshape(-1))
     if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
-    return out
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -120,6 +139,7 @@ class Workload:
     tensors: Tuple[Tuple[str, int, int, str], ...]
     variants: Tuple[Tuple[str, str, str, int], ...]  # (label, rotate, round, seed)
     out_dtype: str = "f32"
+    chunk_rows: int = 0      # > 0: chunked multi-stream recipe (module docstring)
 
     def gemm_mnk(self) -> Tuple[int, int, int]:
         t, o, i = self.tokens, self.out_features, self.in_features
@@ -136,6 +156,21 @@ class Workload:
         return 2 * m * n * k
 
 
+def _values(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
+    """fp32 values of one tensor (or row chunk) before the bf16 rounding."""
+    if kind in ("act", "act_plain"):
+        return rng.standard_normal(size=shape, dtype=np.float32)
+    if kind == "weight":
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x *= np.float32(0.02)
+        return x
+    if kind == "grad":
+        x = rng.standard_t(3.0, size=shape).astype(np.float32)
+        x *= np.float32(1e-4)
+        return x
+    raise ValueError(kind)
+
+
 def _draw(rng: np.random.Generator, rows: int, cols: int, kind: str) -> np.ndarray:
     if kind == "act":
         return activations_bf16(rng, (rows, cols), outlier_frac=0.001)
@@ -148,8 +183,51 @@ def _draw(rng: np.random.Generator, rows: int, cols: int, kind: str) -> np.ndarr
     raise ValueError(kind)
 
 
+OUTLIER_STREAM = 1 << 20     # SeedSequence word of an activation's outlier columns
+CHUNK_ROWS = 512
+
+
+def _gen_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _draw_chunked(data_seed: int, t: int, rows: int, cols: int, kind: str,
+                  chunk_rows: int, pool: ThreadPoolExecutor) -> np.ndarray:
+    """Tensor t of a chunked workload: row chunk j from
+    PCG64(SeedSequence([data_seed, t, j])); outlier columns of an activation
+    from PCG64(SeedSequence([data_seed, t, OUTLIER_STREAM]))."""
+    out = np.empty((rows, cols), np.uint16)
+    cols_x = None
+    if kind == "act":
+        n_out = int(round(0.001 * cols))
+        if n_out > 0:
+            r = np.random.Generator(np.random.PCG64(
+                np.random.SeedSequence([data_seed, t, OUTLIER_STREAM])))
+            cols_x = r.choice(cols, size=n_out, replace=False)
+
+    def chunk(j):
+        lo, hi = j * chunk_rows, min(rows, (j + 1) * chunk_rows)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([data_seed, t, j])))
+        x = _values(rng, (hi - lo, cols), kind)
+        if cols_x is not None:
+            x[:, cols_x] *= np.float32(50.0)
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    list(pool.map(chunk, range(-(-rows // chunk_rows))))
+    return out
+
+
 def workload_tensors(w: Workload) -> Dict[str, np.ndarray]:
-    """Draw the workload's tensors in their listed order from one PCG64 stream."""
+    """Draw the workload's tensors: in their listed order from one PCG64
+    stream, or (chunk_rows > 0) chunk by chunk from per-chunk streams."""
+    if w.chunk_rows > 0:
+        with ThreadPoolExecutor(_gen_threads()) as pool:
+            return {name: _draw_chunked(w.data_seed, t, r, c, kind, w.chunk_rows, pool)
+                    for t, (name, r, c, kind) in enumerate(w.tensors)}
     rng = np.random.Generator(np.random.PCG64(w.data_seed))
     return {name: _draw(rng, r, c, kind) for (name, r, c, kind) in w.tensors}
 
@@ -167,17 +245,17 @@ WORKLOADS: Dict[str, Workload] = {
     "fprop_q_proj": Workload(
         "fprop_q_proj", "fprop", 8192, 4096, 4096, 2,
         (("X", 8192, 4096, "act"), ("W", 4096, 4096, "weight")),
-        (DET, ("det_hadamard16", "hadamard16", "rne", 0)), "bf16"),
+        (DET, ("det_hadamard16", "hadamard16", "rne", 0)), "bf16", CHUNK_ROWS),
     # Wgrad, gate/up: dY 8192x14336 (1e-4 t_3), X 8192x4096 N(0,1).
     "wgrad_gate_proj": Workload(
         "wgrad_gate_proj", "wgrad", 8192, 14336, 4096, 3,
         (("dY", 8192, 14336, "grad"), ("X", 8192, 4096, "act_plain")),
-        (("no_rotation", "none", "rne", 0), DET), "f32"),
+        (("no_rotation", "none", "rne", 0), DET), "f32", CHUNK_ROWS),
     # Dgrad, down_proj: dY 8192x4096 (1e-4 t_3), W 4096x14336.
     "dgrad_down_proj": Workload(
         "dgrad_down_proj", "dgrad", 8192, 4096, 14336, 4,
         (("dY", 8192, 4096, "grad"), ("W", 4096, 14336, "weight")),
-        (DET, ("det_hadamard_sr7", "hadamard", "sr", 7)), "bf16"),
+        (DET, ("det_hadamard_sr7", "hadamard", "sr", 7)), "bf16", CHUNK_ROWS),
 }
 
 BLOCK_TOKENS = 16384
@@ -192,7 +270,8 @@ def block_workloads(tokens: int = BLOCK_TOKENS) -> List[Workload]:
     """All 21 GEMMs of one Llama-3.1-8B block (7 linears x fprop/dgrad/wgrad).
 
     Each linear draws its own X (T x in, with outliers), W (out x in) and
-    dY (T x out) from PCG64(5 * 100 + linear index).
+    dY (T x out) with data seed 5 * 100 + linear index, in row chunks of
+    CHUNK_ROWS (the chunked recipe of the module docstring).
     """
     out: List[Workload] = []
     for li, lin in enumerate(LLAMA_BLOCK_LINEARS):
@@ -203,7 +282,7 @@ def block_workloads(tokens: int = BLOCK_TOKENS) -> List[Workload]:
             out.append(Workload(f"block_{lin.name}_{op}", op, tokens,
                                 lin.out_features, lin.in_features, 500 + li,
                                 tensors, BLOCK_VARIANTS,
-                                "bf16" if op != "wgrad" else "f32"))
+                                "bf16" if op != "wgrad" else "f32", CHUNK_ROWS))
     return out
 
 

@@ -289,6 +289,31 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
                     int64_t ldc, int32_t out_dtype, void *stream);
 
 /* Static, NUL-terminated name of a status code. Never NULL. */
+/*
+ * Dequantize a packed operand to fp32 in its source's shape [rows, cols]:
+ *     out[i][j] = (-1)^sign * E(code) * 2^(s - 127)
+ * with E the E2M1 value of the element's 4-bit code (E4M3 for an MXFP8
+ * operand) and s the E8M0 scale of its 32-element block (36Kr, "Was ist
+ * MXFP4?": one shared exponent per block; the reconstruction formula is
+ * OCP MX's, the standard the pages name in "Fazit"). An axis-0 operand is
+ * written back transposed into [rows, cols], so the output has the source's
+ * orientation either way: the inverse of mx_quantize's encoding, up to its
+ * rounding.
+ *
+ *  q        a descriptor filled by a quantize call; its buffers are read.
+ *  out      device fp32 [rows][ld], ld >= cols (elements), 4-byte aligned;
+ *           written (only the rows x cols elements). Must not overlap q's
+ *           buffers. Caller-owned.
+ *  stream   hipStream_t as void*.
+ * A block with scale 0xFF (a NaN or Inf in the source block) gives NaN in
+ * every element. Every other value is exact in fp32 while finite; values of
+ * magnitude 2^128 or more (scale codes 126 and 127 only, which the
+ * quantizers never write) become +-Inf. Empty operands launch nothing.
+ * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE (ld < cols, or q's extents),
+ * MX_ERR_ALIGN, MX_ERR_UNSUPPORTED (q's size limit), MX_ERR_HIP.
+ */
+mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *stream);
+
 const char *mx_status_string(int32_t status);
 
 /* Static, NUL-terminated library version string. */

@@ -25,7 +25,7 @@ __all__ = [
     "LIB_PATH", "MxError", "QTensorDesc", "QTensor", "load_library", "library_symbols",
     "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "quantize_dual",
     "quantize_pair",
-    "quantize_fp8_sizes", "quantize_fp8", "linear",
+    "quantize_fp8_sizes", "quantize_fp8", "linear", "dequantize",
     "ROTATE", "ROUND", "FORMATS", "OPS", "OUT_DTYPES", "OP_AXES",
 ]
 
@@ -102,6 +102,8 @@ _SIGNATURES = {
     "mx_linear": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(QTensorDesc),
                                  ctypes.POINTER(QTensorDesc), ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_void_p]),
+    "mx_dequantize": (ctypes.c_int, [ctypes.POINTER(QTensorDesc), ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p]),
     "mx_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "mx_version": (ctypes.c_char_p, []),
     "mx_last_hip_error": (ctypes.c_char_p, []),
@@ -354,4 +356,23 @@ def linear(op: str, A: QTensor, B: QTensor, out_dtype: str = "f32", out=None,
                        out.data_ptr() if out.numel() else None, ldc, OUT_DTYPES[out_dtype],
                        _stream_handle(A.codes.device, stream))
     _check(st, "mx_linear")
+    return out
+
+
+def dequantize(q: QTensor, out=None, stream=None):
+    """fp32 values of a quantized operand in its source's shape [rows, cols]
+    (see mx_dequantize): sign * E2M1 (or E4M3) value * 2^(scale - 127)."""
+    import torch
+    lib = load_library()
+    rows, cols = q.source_shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=q.codes.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or tuple(out.shape) != (rows, cols):
+        raise ValueError("out must be a float32 tensor of the source's shape")
+    if out.numel() and out.stride(1) != 1:
+        raise ValueError("out must have unit column stride")
+    ld = out.stride(0) if rows > 1 else max(cols, 1)
+    st = lib.mx_dequantize(ctypes.byref(q.desc), out.data_ptr() if out.numel() else None, ld,
+                           _stream_handle(q.codes.device, stream))
+    _check(st, "mx_dequantize")
     return out

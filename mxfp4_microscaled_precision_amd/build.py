@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libmxfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_gemm_e4m3.hip", "mx_api.cpp"]
+SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_gemm_e4m3.hip", "mx_dequant.hip", "mx_api.cpp"]
 
 # -ffp-contract=off: the rotation's adds and multiplies must round one by one.
 # -packed-fp32-ops off: packed fp32 VALU forms are not used by this library.

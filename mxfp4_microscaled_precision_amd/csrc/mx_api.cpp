@@ -314,6 +314,25 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
                                                  : mx::gemm_launch(g, s));
 }
 
+mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *stream) {
+  const mx_status st = check_qtensor(q);
+  if (st != MX_OK) return st;
+  if (ld < q->cols) return MX_ERR_SHAPE;
+  if (q->rows == 0 || q->cols == 0) return MX_OK;
+  if (out == nullptr) return MX_ERR_NULL;
+  if (!aligned(out, 4)) return MX_ERR_ALIGN;
+  mx::DequantArgs a;
+  a.codes = static_cast<const uint8_t *>(q->codes);
+  a.scales = static_cast<const uint8_t *>(q->scales);
+  operand_extents(q, &a.mn, &a.k);
+  padded_extents(q->rows, q->cols, q->axis, &a.mnp, &a.kp);
+  a.axis = q->axis;
+  a.fmt = q->format == MX_FMT_FP8_E4M3 ? 1 : 0;
+  a.out = out;
+  a.ld = ld;
+  return hip_status(mx::dequantize_launch(a, static_cast<hipStream_t>(stream)));
+}
+
 const char *mx_status_string(int32_t status) {
   switch (status) {
     case MX_OK: return "MX_OK";

@@ -80,4 +80,16 @@ hipError_t gemm_e4m3_launch(const GemmArgs &g, hipStream_t stream);
 // Compute units of the current device (one persistent GEMM workgroup each).
 int cu_count();
 
+// fp32 values of a packed operand in its source's shape.
+struct DequantArgs {
+  const uint8_t *codes, *scales;   // tiled (E2M1 or E4M3 codes)
+  int64_t mn, k, mnp, kp;          // operand extents and their padded ones
+  int axis;                        // source orientation: 1 -> [mn][k], 0 -> [k][mn]
+  int fmt;                         // 0: E2M1, 1: E4M3
+  float *out;                      // leading dimension ld
+  int64_t ld;
+};
+
+hipError_t dequantize_launch(const DequantArgs &a, hipStream_t stream);
+
 }  // namespace mx

@@ -71,6 +71,10 @@ What pins each function (tests/test_oracle_*.py, all "not gpu"):
                         re-quantizing a representable block is a fixed point.
   tile_codes/scales     element-by-element address formula written out in a
                         test loop; round trip through untile_*.
+  operand_mse           exhaustive search for the nearest E2M1 value of every
+                        element under its block scale (the error RNE must
+                        reach); zero on representable blocks; the one-hot
+                        block's exact error (0.1875 - c)^2.
   dequantize_ref,
   mx_gemm_ref           explicit triple loop and exact fractions.Fraction sums;
                         the rotation cancels in the product.
@@ -117,6 +121,7 @@ __all__ = [
     "untile_codes",
     "untile_scales",
     "mx_gemm_ref",
+    "operand_mse",
     "linear_ref",
     "bf16_round_ref",
     "fwht16x2_f32",
@@ -635,6 +640,17 @@ def mx_gemm_ref(qa: QuantRef, qb: QuantRef) -> np.ndarray:
     da = dequantize_ref(qa.codes, qa.scales, qa.fmt)
     db = dequantize_ref(qb.codes, qb.scales, qb.fmt)
     return da @ db.T
+
+
+def operand_mse(q: QuantRef) -> float:
+    """Operand-level quantization error: mean over the operand of
+    (deq - y)^2 in fp64, y the rotated values that were quantized and deq
+    their dequantized codes ([36Kr] "Fehlerdiagnoseexperiment": the
+    quantization error of the Wgrad operands with and without the rotation).
+    R is orthonormal, so this is also the error in the source's own domain,
+    up to the fp32 rounding of y."""
+    d = dequantize_ref(q.codes, q.scales, q.fmt) - np.asarray(q.rotated, np.float64)
+    return float(np.mean(d * d))
 
 
 def linear_ref(op: str, a_src: np.ndarray, b_src: np.ndarray, rotate: str = ROT_HADAMARD,

@@ -252,3 +252,19 @@ def test_linear_empty_is_a_noop():
     lib = mx.load_library()
     assert _lin(lib, 0, _desc(0, 128, 1), _desc(96, 128, 1), C=None) == 0
     assert _lin(lib, 2, _desc(64, 0, 0), _desc(64, 32, 0), C=None) == 0
+
+
+def test_dequantize_rejects_before_launch():
+    lib = mx.load_library()
+    deq = lambda d, out=4096, ld=None: lib.mx_dequantize(  # noqa: E731
+        ctypes.byref(d), out, d.cols if ld is None else ld, None)
+    assert lib.mx_dequantize(None, 4096, 128, None) == -1
+    assert deq(_desc(64, 128, 1), ld=127) == -2           # ld < cols
+    assert deq(_desc(64, 128, 1), out=None) == -1
+    assert deq(_desc(64, 128, 1), out=4098) == -3         # fp32 out not 4-byte aligned
+    assert deq(_desc(64, 48, 1)) == -2                    # K % 32
+    assert deq(_desc(64, 128, 2)) == -4                   # bad axis
+    assert deq(_desc(64, 128, 1, codes=None)) == -1
+    assert deq(_desc(64, 128, 1, fmt=3)) == -4
+    assert deq(_desc(1 << 17, 1 << 14, 1)) == -6          # beyond the size limit
+    assert deq(_desc(0, 128, 1), out=None) == 0           # empty: nothing launched

@@ -2,8 +2,10 @@
 
 Bar: E2M1 codes and E8M0 scales bit-exact (stochastic rounding included, for
 a given seed); GEMM outputs within 1e-5 relative Frobenius error of the fp64
-oracle GEMM over the dequantized operands; bf16 outputs equal to the
-round-to-nearest-even of the same GEMM's fp32 output.
+oracle GEMM over the dequantized operands, and every element within
+(K/32 + 4) 2^-23 sum_k |a b| of it (fp32 accumulation of exact block sums);
+bf16 outputs equal to the round-to-nearest-even of the same GEMM's fp32
+output.
 """
 import numpy as np
 import pytest
@@ -11,6 +13,7 @@ import pytest
 import oracle
 from datagen import (WORKLOADS, f32_to_bf16_bits, operands_for, workload_tensors)
 from gpu_util import host_u8, rel_fro, to_dev, to_dev_strided
+from oracle_util import oracle_operand
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +39,18 @@ def _check_q(q_gpu, ref, what=""):
     bad = np.count_nonzero(codes != want_codes)
     bad_s = np.count_nonzero(scales != want_scales)
     assert bad == 0 and bad_s == 0, f"{what}: {bad} code bytes, {bad_s} scales differ"
+
+
+def _check_elementwise(got, C_ref, ra, rb, what=""):
+    """Every element within (K/32 + 4) 2^-23 sum_k |a b| of the fp64 product:
+    fp32 accumulation of K/128 exactly summed MFMA blocks, with a wide
+    margin."""
+    da = np.abs(oracle.dequantize_ref(ra.codes, ra.scales, ra.fmt))
+    db = np.abs(oracle.dequantize_ref(rb.codes, rb.scales, rb.fmt))
+    k = ra.codes.shape[1]
+    bound = (k / 32 + 4) * 2.0 ** -23 * (da @ db.T)
+    over = np.count_nonzero(np.abs(np.asarray(got, np.float64) - C_ref) > bound)
+    assert over == 0, f"{what}: {over} elements beyond the per-element bound"
 
 
 def _rand_bits(rng, shape, scale=1.0):
@@ -213,6 +228,7 @@ def _gemm_case(mx, op, a_src, b_src, rot, rnd, seed, check_bf16=True):
     got = c32.cpu().numpy()
     err = rel_fro(got, C_ref)
     assert err <= GEMM_TOL, f"{op} {rot} {rnd}: rel Frobenius {err:.3e}"
+    _check_elementwise(got, C_ref, ra, rb, f"{op} {rot} {rnd}")
     if check_bf16:
         import torch
         b16 = c16.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -342,12 +358,23 @@ FULL = [("fprop_q_proj", "det_hadamard"), ("fprop_q_proj", "det_hadamard16"),
         ("dgrad_down_proj", "det_hadamard_sr7")]
 
 
+def _tile_cover(M, N):
+    """256 x 256 output tiles such that every tile row and every tile column
+    holds at least one whole tile: (i, i mod tn) and (j mod tm, j)."""
+    tm, tn = -(-M // 256), -(-N // 256)
+    return sorted({(i, i % tn) for i in range(tm)} | {(j % tm, j) for j in range(tn)})
+
+
 @pytest.mark.parametrize("name,variant", FULL)
 def test_full_size_sampled(mx, name, variant):
-    """Full workload sizes in the launch configuration the bench times;
-    sampled operand rows are checked bit for bit and the sampled output
-    block C[ms, ns] against the oracle."""
+    """Full workload sizes in the launch configuration the bench times: both
+    whole operands bit-exact against the oracle (codes and scales, padding
+    excluded); the output on a set of whole 256 x 256 tiles covering every
+    tile row and tile column within the per-element bound and 1e-5 relative
+    Frobenius error; the bf16 epilogue over the whole output."""
+    import torch
     w = WORKLOADS[name]
+    print(f"[full] {name} {variant}", flush=True)
     _, rot, rnd, seed = [v for v in w.variants if v[0] == variant][0]
     t = workload_tensors(w)
     a_src, ax_a, b_src, ax_b = operands_for(w, t)
@@ -356,54 +383,124 @@ def test_full_size_sampled(mx, name, variant):
     qb = mx.quantize(to_dev(b_src), ax_b, rot, rnd, seed=seed_b)
     c = mx.linear(w.op, qa, qb, "f32")
     _sync()
-    rng = np.random.default_rng(5)
     M, N = qa.mn, qb.mn
-    ms = np.sort(rng.choice(M, 48, replace=False))
-    ns = np.sort(rng.choice(N, 48, replace=False))
-
-    def ref_rows(src, axis, idx, s):
-        if axis == 1:
-            return oracle.quantize_ref(src[idx], 1, rotate=rot, rounding=rnd, seed=s,
-                                       row_index=idx, total_cols=src.shape[1])
-        return oracle.quantize_ref(src[:, idx], 0, rotate=rot, rounding=rnd, seed=s,
-                                   col_index=idx, total_cols=src.shape[1])
-
-    ra = ref_rows(a_src, ax_a, ms, seed_a)
-    rb = ref_rows(b_src, ax_b, ns, seed_b)
-    ga = oracle.untile_codes(host_u8(qa.codes), M, qa.k)
-    gsa = oracle.untile_scales(host_u8(qa.scales), M, qa.k)
-    gb = oracle.untile_codes(host_u8(qb.codes), N, qb.k)
-    gsb = oracle.untile_scales(host_u8(qb.scales), N, qb.k)
-    assert np.array_equal(ga[ms], ra.codes) and np.array_equal(gsa[ms], ra.scales)
-    assert np.array_equal(gb[ns], rb.codes) and np.array_equal(gsb[ns], rb.scales)
-    C_ref = oracle.mx_gemm_ref(ra, rb)
+    ra = oracle_operand(a_src, ax_a, rot, rnd, seed_a)
+    rb = oracle_operand(b_src, ax_b, rot, rnd, seed_b)
+    for q, r, nm in ((qa, ra, "A"), (qb, rb, "B")):
+        codes = oracle.untile_codes(host_u8(q.codes), q.mn, q.k)
+        scales = oracle.untile_scales(host_u8(q.scales), q.mn, q.k)
+        nb, ns = np.count_nonzero(codes != r.codes), np.count_nonzero(scales != r.scales)
+        assert nb == 0 and ns == 0, f"{name}/{variant} {nm}: {nb} codes, {ns} scales differ"
+        del codes, scales
     c_host = c.cpu().numpy()
-    got = c_host[np.ix_(ms, ns)]
-    err = rel_fro(got, C_ref)
+    got_all, ref_all = [], []
+    for ti, tj in _tile_cover(M, N):
+        rs, cs = slice(256 * ti, min(M, 256 * ti + 256)), slice(256 * tj, min(N, 256 * tj + 256))
+        sa_ = oracle.QuantRef(ra.codes[rs], ra.scales[rs], np.empty((0, 0), np.float32), ax_a)
+        sb_ = oracle.QuantRef(rb.codes[cs], rb.scales[cs], np.empty((0, 0), np.float32), ax_b)
+        C_ref = oracle.mx_gemm_ref(sa_, sb_)
+        got = c_host[rs, cs]
+        _check_elementwise(got, C_ref, sa_, sb_, f"{name}/{variant} tile ({ti}, {tj})")
+        got_all.append(got.astype(np.float64).ravel())
+        ref_all.append(C_ref.ravel())
+    err = rel_fro(np.concatenate(got_all), np.concatenate(ref_all))
     assert err <= GEMM_TOL, f"{name}/{variant}: rel Frobenius {err:.3e}"
     if w.out_dtype == "bf16":
         # the bf16 epilogue over the whole output: RNE of the fp32 result
         cb = mx.linear(w.op, qa, qb, "bf16")
         _sync()
-        got_b = cb.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+        got_b = cb.cpu().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got_b, oracle.bf16_round_ref(c_host))
 
 
 # ------------------------------------------------- structural-error harness
-def test_structural_error_harness_separates_fixed_and_changing_errors(mx):
-    """The repeated-Wgrad harness on a small problem: with a deterministic
-    rotation every step reproduces the same dW bit for bit, so the error of
-    the K-step mean equals the single-step error; with a new seed per step
-    (random signs, stochastic rounding) the mean's error falls below it."""
+def test_structural_error_harness_against_the_oracle(mx):
+    """The repeated-Wgrad harness on a small problem, anchored on the oracle:
+    for every variant and its first three steps, the quantized operands the
+    harness used are bit-exact against oracle.linear_ref with the step's seed
+    (seed k for the randomized variants, 0 otherwise; B takes k | 1 << 32)
+    and each dW_k lies within 1e-5 of the oracle's product; the harness's
+    reported errors (single-step and the 2-step mean, against the exact
+    product of the bf16 operands) equal those recomputed from the oracle's
+    dW_k within 1e-4 relative. Then the property the harness measures: a
+    deterministic rotation reproduces dW bit for bit every step, so the
+    K-step mean keeps the single-step error; a new seed per step (random
+    signs, stochastic rounding) lets the mean's error fall."""
     import bench
-    res = bench.structural_error(mx, T=1024, n_out=256, n_in=128, steps=16)
+    T, n_out, n_in = 512, 160, 96
+    res = bench.structural_error(mx, T=T, n_out=n_out, n_in=n_in, steps=16, keep_steps=3)
+    dY, X = bench.structural_inputs(T, n_out, n_in)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    exact = f(dY).T @ f(X)
+    ex_norm = np.linalg.norm(exact)
+    for label, rot, rnd, reseed in bench.STRUCTURAL_VARIANTS:
+        steps = res["_steps"][label]
+        refs = []
+        for k, st in enumerate(steps, start=1):
+            seed = bench.structural_step_seed(k, reseed)
+            assert st["seed"] == seed
+            C_ref, ra, rb = oracle.linear_ref("wgrad", dY, X, rotate=rot, rounding=rnd, seed=seed)
+            want_a = (oracle.tile_codes(ra.codes), oracle.tile_scales(ra.scales, T))
+            want_b = (oracle.tile_codes(rb.codes), oracle.tile_scales(rb.scales, T))
+            assert np.array_equal(st["a_codes"], want_a[0]) and np.array_equal(st["a_scales"], want_a[1]), (label, k)
+            assert np.array_equal(st["b_codes"], want_b[0]) and np.array_equal(st["b_scales"], want_b[1]), (label, k)
+            err = rel_fro(st["dW"], C_ref)
+            assert err <= GEMM_TOL, f"{label} step {k}: rel Frobenius {err:.3e}"
+            refs.append(C_ref)
+        v = res["variants"][label]
+        want_single = [np.linalg.norm(r - exact) / ex_norm for r in refs]
+        want_mean2 = np.linalg.norm((refs[0] + refs[1]) / 2 - exact) / ex_norm
+        assert np.allclose(v["single_step_rel_err"][:3], want_single, rtol=1e-4), label
+        assert abs(v["mean_rel_err"]["2"] - want_mean2) <= 1e-4 * want_mean2, label
     v = res["variants"]
     for det in ("det_hadamard", "det_hadamard16"):
-        s = v[det]["single_step_rel_err"]
-        assert len(set(s)) == 1, det
-        assert abs(v[det]["mean_rel_err"]["16"] - s[0]) <= 1e-6 * s[0], det
+        s_ = v[det]["single_step_rel_err"]
+        assert len(set(s_)) == 1, det
+        assert abs(v[det]["mean_rel_err"]["16"] - s_[0]) <= 1e-6 * s_[0], det
+        dws = [st["dW"] for st in res["_steps"][det]]
+        assert all(np.array_equal(dws[0], d) for d in dws[1:]), det
     for rnd in ("rand_sign_hadamard", "no_rotation_sr", "hadamard_sr"):
         assert v[rnd]["mean_rel_err"]["16"] < 0.7 * v[rnd]["single_step_rel_err"][0], rnd
+
+
+# ----------------------------------------------------------- dequantization
+@pytest.mark.parametrize("fmt", ["fp4_e2m1", "fp8_e4m3"])
+@pytest.mark.parametrize("axis", [1, 0])
+def test_dequantize_matches_oracle(mx, fmt, axis):
+    """mx_dequantize against the oracle's dequantization of the oracle's
+    codes, bit for bit (every value is exact in fp32): a ragged operand in
+    its source orientation, a row-strided output whose pad columns stay
+    untouched, and NaN / zero / denormal blocks."""
+    import torch
+    rng = np.random.default_rng(88 + axis)
+    shape = (300, 224) if axis == 1 else (224, 300)
+    x = _rand_bits(rng, shape, 2.0)
+    f = np.float32
+    specials = f32_to_bf16_bits(np.stack([np.zeros(32, f), np.r_[np.ones(31, f), f(np.nan)],
+                                          np.full(32, 1e-39, f)]))
+    if axis == 1:
+        x[:3, :32] = specials
+    else:
+        x[:32, :3] = specials.T
+    xd = to_dev(x)
+    if fmt == "fp4_e2m1":
+        q = mx.quantize(xd, axis, "hadamard", "sr", seed=5)
+        ref = oracle.quantize_ref(x, axis, rotate="hadamard", rounding="sr", seed=5)
+    else:
+        q = mx.quantize_fp8(xd, axis, "hadamard", seed=5)
+        ref = oracle.quantize_ref(x, axis, rotate="hadamard", fmt="fp8_e4m3", seed=5)
+    want = oracle.dequantize_ref(ref.codes, ref.scales, ref.fmt).astype(np.float32)   # [MN, K]
+    if axis == 0:
+        want = np.ascontiguousarray(want.T)
+    got = mx.dequantize(q)
+    big = torch.full((shape[0], shape[1] + 5), 7.0, dtype=torch.float32, device="cuda")
+    mx.dequantize(q, out=big[:, :shape[1]])
+    _sync()
+    g = got.cpu().numpy()
+    assert np.array_equal(np.isnan(g), np.isnan(want)) and np.isnan(want).any()
+    assert np.array_equal(np.nan_to_num(g).view(np.uint32), np.nan_to_num(want).view(np.uint32))
+    assert torch.equal(big[:, :shape[1]].nan_to_num(), got.nan_to_num())
+    assert torch.all(big[:, shape[1]:] == 7.0)
 
 
 def test_quantize_axis1_many_tiles_ragged(mx):
