@@ -40,10 +40,12 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
+    // the two three-way xors as one v_bitop3_b32 each (truth table 0x96:
+    // odd parity of the three inputs)
     U4 n;
-    n.x = hi1 ^ c.y ^ k0;
+    n.x = __builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96);
     n.y = lo1;
-    n.z = hi0 ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96);
     n.w = lo0;
     c = n;
     k0 += 0x9E3779B9u;
