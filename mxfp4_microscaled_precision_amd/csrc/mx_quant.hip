@@ -164,19 +164,27 @@ __device__ __forceinline__ uint32_t quantize_block(const float (&v)[32],
     const float p = pow2_neg(e);
 #pragma unroll
     for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], c), p);
-  } else if (__builtin_expect(!__any(e > 123), 1)) {
-    // c * 2^-e is an exact normal number for e <= 123: one multiply gives
-    // the bits of fl32(fl32(h * c) * 2^-e)
-    const float ce = __fmul_rn(c, pow2_neg(e));
-#pragma unroll
-    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(v[i], ce);
   } else {
-    // some lane of the wave has |y| >= 2^126: the two multiplies, for all
+    // c * 2^-e is an exact normal number for e <= 123: one multiply gives
+    // the bits of fl32(fl32(h * c) * 2^-e). If some lane of the wave has
+    // |y| >= 2^126 (e > 123), the wave multiplies twice: such a lane by c,
+    // then by 2^-e, as written; the other lanes by c_e, then by 1, which
+    // changes nothing. The first multiply overwrites a copy of v in place,
+    // so only one array of 32 is live (a separate array for each case cost
+    // 26 more registers in the dual kernel and one wave per SIMD).
     const float ce = __fmul_rn(c, pow2_neg(min(e, 123)));
-    const float m1 = e > 123 ? c : ce;
-    const float m2 = e > 123 ? pow2_neg(e) : 1.0f;
+    float h[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(__fmul_rn(v[i], m1), m2);
+    for (int i = 0; i < 32; ++i) h[i] = v[i];
+    float mult = ce;
+    if (__builtin_expect(__any(e > 123), 0)) {
+      const float m1 = e > 123 ? c : ce;
+      mult = e > 123 ? pow2_neg(e) : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) h[i] = __fmul_rn(h[i], m1);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) t[i] = __fmul_rn(h[i], mult);
   }
   if constexpr (FMT == kFmtE4M3) {
     // v_cvt_scalef32_pk_fp8_f32 at scale 1.0 rounds to the nearest E4M3
