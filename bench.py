@@ -710,7 +710,13 @@ def main():
             },
             "gemm_all": {"tflops": round(g_all_fl / (g_all_us * 1e-6) / 1e12, 2),
                          "frac": round(g_all_fl / (g_all_us * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4)},
-            "per_kernel_us": {k: round(v["us"], 1) for k, v in split.items()},
+            # the step's time split over the kernel classes in proportion to
+            # their event-timed durations (so the split sums to ms_per_step);
+            # the raw event-timed sums are per_kernel_us_events: an event
+            # between every two launches adds a few us to each
+            "per_kernel_us": {k: round(v["us"] * h["ms_per_step"] / inst_ms, 1)
+                              for k, v in split.items()},
+            "per_kernel_us_events": {k: round(v["us"], 1) for k, v in split.items()},
             "instrumented_ms_per_step": round(inst_ms, 5),
             "per_op": per_op,
             "variants": {lb: {"ms_per_step": round(v["ms_per_step"], 5),
