@@ -175,8 +175,28 @@ class BlockRunner:
                               "outs": outs})
             print(f"[bench] block {lin.name}: {T}x{i} -> {o} resident", file=sys.stderr,
                   flush=True)
+        # Linears that see their inputs together share one grouped GEMM launch
+        # per op (mx_linear_batched): k and v read the same activations, gate
+        # and up too. Each (tensor, axis) descriptor feeds exactly one op, so a
+        # group's descriptors live side by side in one ctypes array per
+        # (tensor, axis): the quantizer fills element j, the GEMM takes the array.
+        by_name = {L["name"]: L for L in self.lins}
+        self.groups = []
+        for names in self.GROUPS:
+            ls = [by_name[n] for n in names]
+            descs = {}
+            for key in ls[0]["bufs"]:
+                arr = (mx.QTensorDesc * len(ls))()
+                for j, L in enumerate(ls):
+                    c, s, _ = L["bufs"][key]
+                    L["bufs"][key] = (c, s, arr[j])
+                descs[key] = arr
+            self.groups.append({"lins": ls, "descs": descs})
         torch.cuda.synchronize()
         self.calls = []
+
+    GROUPS = (("q_proj",), ("k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"),
+              ("down_proj",))
 
     # (A, B) of each op as (tensor, axis), and the output dtype
     OPS = (("fprop", ("X", 1), ("W", 1), "bf16"), ("dgrad", ("dY", 1), ("W", 0), "bf16"),
@@ -201,39 +221,60 @@ class BlockRunner:
         R, D = mx.ROTATE[rot], mx.ROUND[rnd]
         seeds = self._seeds(seed)
         calls = []
-        for L in self.lins:
-            src, bufs = L["src"], L["bufs"]
 
-            def qargs(k, axis):
-                x = src[k]
-                c, s, d = bufs[k, axis]
-                sd = seeds[k][0] if axis == 1 else seeds[k][1]
-                return (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), axis, 32, R, D, sd,
-                        c.data_ptr(), s.data_ptr(), ctypes.byref(d), st)
+        def dual(L, k):
+            x, bufs = L["src"][k], L["bufs"]
+            c1, s1, d1 = bufs[k, 1]
+            c0, s0, d0 = bufs[k, 0]
+            return ("quant_dual", {"linear": L["name"], "tensor": k, "elems": x.numel()},
+                    lib.mx_quantize_dual,
+                    (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), 32, R, D, seeds[k][0],
+                     seeds[k][1], c1.data_ptr(), s1.data_ptr(), c0.data_ptr(), s0.data_ptr(),
+                     ctypes.byref(d1), ctypes.byref(d0), st))
 
-            def gemm(op, a, b, odt):
-                C = L["outs"][op]
-                m, n = C.shape
-                k = self.T if op == "wgrad" else (L["in"] if op == "fprop" else L["out"])
-                return ("gemm_" + odt, {"linear": L["name"], "op": op, "M": m, "N": n, "K": k},
-                        lib.mx_linear, (mx.OPS[op], ctypes.byref(bufs[a][2]),
-                                        ctypes.byref(bufs[b][2]), C.data_ptr(), C.stride(0),
-                                        mx.OUT_DTYPES[odt], st))
+        def gemm_info(ls, op):
+            C = ls[0]["outs"][op]
+            m, n = C.shape
+            L = ls[0]
+            k = self.T if op == "wgrad" else (L["in"] if op == "fprop" else L["out"])
+            return {"linear": "+".join(x["name"] for x in ls), "op": op, "M": m, "N": n, "K": k,
+                    "count": len(ls)}
 
-            if not per_op:
-                for k in ("X", "W", "dY"):
-                    x = src[k]
-                    c1, s1, d1 = bufs[k, 1]
-                    c0, s0, d0 = bufs[k, 0]
-                    calls.append(("quant_dual", {"linear": L["name"], "tensor": k,
-                                                 "elems": x.numel()}, lib.mx_quantize_dual,
-                                  (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), 32, R, D,
-                                   seeds[k][0], seeds[k][1], c1.data_ptr(), s1.data_ptr(),
-                                   c0.data_ptr(), s0.data_ptr(), ctypes.byref(d1),
-                                   ctypes.byref(d0), st)))
+        def gemm(L, op, a, b, odt):
+            C = L["outs"][op]
+            bufs = L["bufs"]
+            return ("gemm_" + odt, gemm_info([L], op),
+                    lib.mx_linear, (mx.OPS[op], ctypes.byref(bufs[a][2]),
+                                    ctypes.byref(bufs[b][2]), C.data_ptr(), C.stride(0),
+                                    mx.OUT_DTYPES[odt], st))
+
+        def gemm_group(grp, op, a, b, odt):
+            ls = grp["lins"]
+            cs = (ctypes.c_void_p * len(ls))(*[L["outs"][op].data_ptr() for L in ls])
+            return ("gemm_" + odt, gemm_info(ls, op),
+                    lib.mx_linear_batched, (mx.OPS[op], len(ls), grp["descs"][a],
+                                            grp["descs"][b], cs, ls[0]["outs"][op].stride(0),
+                                            mx.OUT_DTYPES[odt], st))
+
+        if not per_op:
+            for grp in self.groups:
+                for L in grp["lins"]:
+                    for k in ("X", "W", "dY"):
+                        calls.append(dual(L, k))
                 for op, a, b, odt in self.OPS:
-                    calls.append(gemm(op, a, b, odt))
-            else:
+                    calls.append(gemm(grp["lins"][0], op, a, b, odt) if len(grp["lins"]) == 1
+                                 else gemm_group(grp, op, a, b, odt))
+        else:
+            for L in self.lins:
+                src, bufs = L["src"], L["bufs"]
+
+                def qargs(k, axis):
+                    x = src[k]
+                    c, s, d = bufs[k, axis]
+                    sd = seeds[k][0] if axis == 1 else seeds[k][1]
+                    return (x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), axis, 32, R, D, sd,
+                            c.data_ptr(), s.data_ptr(), ctypes.byref(d), st)
+
                 for op, a, b, odt in self.OPS:
                     if op == "fprop":
                         x, w = src["X"], src["W"]
@@ -252,7 +293,7 @@ class BlockRunner:
                                                            "axis": axis,
                                                            "elems": src[k].numel()},
                                           lib.mx_quantize, qargs(k, axis)))
-                    calls.append(gemm(op, a, b, odt))
+                    calls.append(gemm(L, op, a, b, odt))
         self.calls = calls
         return calls
 
@@ -313,12 +354,13 @@ def block_bench(mx, args):
         d["us"] += ms * 1e3
         d["launches"] += 1
         if kind.startswith("gemm"):
-            f = 2.0 * info["M"] * info["N"] * info["K"]
+            f = 2.0 * info["M"] * info["N"] * info["K"] * info["count"]
             d["flops"] += f
-            d["bytes"] += gemm_bytes(info["M"], info["N"], info["K"], 2 if kind == "gemm_bf16" else 4)
+            d["bytes"] += info["count"] * gemm_bytes(info["M"], info["N"], info["K"],
+                                                     2 if kind == "gemm_bf16" else 4)
             per_op[f"{info['linear']}/{info['op']}"] = {
-                "M": info["M"], "N": info["N"], "K": info["K"], "us": round(ms * 1e3, 2),
-                "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+                "M": info["M"], "N": info["N"], "K": info["K"], "gemms": info["count"],
+                "us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
         else:
             d["bytes"] += info["elems"] * (2 + 2 * (0.5 + 1.0 / 32))
     return br, res, head, split, per_op, inst_ms
@@ -676,7 +718,8 @@ def main():
                      "no real weights or data)"),
             "config": {
                 "workload": (f"Llama-3.1-8B block T={br.T}: 7 linears x Fprop/Dgrad/Wgrad "
-                             f"(21 MXFP4 GEMMs), {head}, each of X/W/dY quantized once "
+                             f"(21 MXFP4 GEMMs; k/v and gate/up each in one grouped launch per "
+                             f"op), {head}, each of X/W/dY quantized once "
                              f"into both orientations"),
                 "tokens": br.T, "variant": head, "gemms": 21,
                 "gflop_per_step": round(flops / 1e9, 1),
@@ -685,7 +728,7 @@ def main():
             "pct_mfma_peak": round(100.0 * h["tflops"] / PEAK_FP4_TFLOPS, 2),
             "roofline": {
                 "kernel": "gemm_tiled_kernel<1, 0> (MXFP4 GEMM, bf16 out: the 14 Fprop and "
-                          "Dgrad GEMMs of a step)",
+                          "Dgrad GEMMs of a step, in 10 launches with k/v and gate/up grouped)",
                 "bound": "mfma",
                 "achieved": round(dom_ach, 2),
                 "peak": PEAK_FP4_TFLOPS,

@@ -288,7 +288,30 @@ mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_
 mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C,
                     int64_t ldc, int32_t out_dtype, void *stream);
 
-/* Static, NUL-terminated name of a status code. Never NULL. */
+/*
+ * count GEMMs of one op and one shape in a single launch (a grouped GEMM):
+ *     C[i] = mx_linear(op, &A[i], &B[i])    for i < count
+ * The Fprop, Dgrad or Wgrad of several linears that see their inputs at the
+ * same time (the k and v projections of an attention block, which read the
+ * same activations; the gate and up projections of its feed-forward layer),
+ * as in mx_linear (36Kr, "Fehlerdiagnoseexperiment": the three GEMMs of every
+ * linear). Small GEMMs fill the compute units together where each alone
+ * would leave some idle. Each C[i] is bitwise identical to what mx_linear
+ * writes for the same pair.
+ *  A, B     host arrays of count descriptors, MXFP4 (E2M1) operands only.
+ *           Every A[i] must have A[0]'s rows, cols and axis, every B[i]
+ *           B[0]'s (else MX_ERR_SHAPE); each pair must satisfy mx_linear's
+ *           rules for op.
+ *  C        host array of count device pointers, each row-major [M][N] with
+ *           the shared leading dimension ldc; written; no C[i] may overlap
+ *           another C[j] or any operand.
+ *  count    1 .. 4 (else MX_ERR_ARG).
+ * Requirements and errors otherwise as for mx_linear; an MXFP8 operand gives
+ * MX_ERR_UNSUPPORTED. Nothing is launched unless every entry is valid.
+ */
+mx_status mx_linear_batched(int32_t op, int32_t count, const mx_qtensor *A, const mx_qtensor *B,
+                            void *const *C, int64_t ldc, int32_t out_dtype, void *stream);
+
 /*
  * Dequantize a packed operand to fp32 in its source's shape [rows, cols]:
  *     out[i][j] = (-1)^sign * E(code) * 2^(s - 127)
@@ -314,6 +337,7 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
  */
 mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *stream);
 
+/* Static, NUL-terminated name of a status code. Never NULL. */
 const char *mx_status_string(int32_t status);
 
 /* Static, NUL-terminated library version string. */

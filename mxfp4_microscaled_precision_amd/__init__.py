@@ -25,7 +25,7 @@ __all__ = [
     "LIB_PATH", "MxError", "QTensorDesc", "QTensor", "load_library", "library_symbols",
     "status_string", "version", "last_hip_error", "quantize_sizes", "quantize", "quantize_dual",
     "quantize_pair",
-    "quantize_fp8_sizes", "quantize_fp8", "linear", "dequantize",
+    "quantize_fp8_sizes", "quantize_fp8", "linear", "linear_batched", "dequantize",
     "ROTATE", "ROUND", "FORMATS", "OPS", "OUT_DTYPES", "OP_AXES",
 ]
 
@@ -102,6 +102,10 @@ _SIGNATURES = {
     "mx_linear": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(QTensorDesc),
                                  ctypes.POINTER(QTensorDesc), ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_void_p]),
+    "mx_linear_batched": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(QTensorDesc), ctypes.POINTER(QTensorDesc),
+                                         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_void_p]),
     "mx_dequantize": (ctypes.c_int, [ctypes.POINTER(QTensorDesc), ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_void_p]),
     "mx_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -357,6 +361,39 @@ def linear(op: str, A: QTensor, B: QTensor, out_dtype: str = "f32", out=None,
                        _stream_handle(A.codes.device, stream))
     _check(st, "mx_linear")
     return out
+
+
+def linear_batched(op: str, As, Bs, out_dtype: str = "f32", outs=None, stream=None):
+    """Several GEMMs of one op and one shape in one launch (see
+    mx_linear_batched): C[i] = linear(op, As[i], Bs[i]); returns the list of
+    C [M, N] (fp32 or bf16), bitwise identical to separate linear calls."""
+    import torch
+    lib = load_library()
+    n = len(As)
+    if len(Bs) != n:
+        raise ValueError("As and Bs differ in length")
+    M, N = As[0].mn, Bs[0].mn
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=dt, device=As[0].codes.device) for _ in range(n)]
+    if len(outs) != n:
+        raise ValueError("outs differs in length")
+    lds = set()
+    for o in outs:
+        if o.dtype != dt or o.dim() != 2 or tuple(o.shape) != (M, N):
+            raise ValueError("an output has the wrong dtype or shape")
+        if o.numel() and o.stride(1) != 1:
+            raise ValueError("outputs must have unit column stride")
+        lds.add(o.stride(0) if M > 1 else max(N, 4))
+    if len(lds) != 1:
+        raise ValueError("outputs must share one leading dimension")
+    da = (QTensorDesc * n)(*[q.desc for q in As])
+    db = (QTensorDesc * n)(*[q.desc for q in Bs])
+    cs = (ctypes.c_void_p * n)(*[o.data_ptr() if o.numel() else None for o in outs])
+    st = lib.mx_linear_batched(OPS[op], n, da, db, cs, lds.pop(), OUT_DTYPES[out_dtype],
+                               _stream_handle(As[0].codes.device, stream))
+    _check(st, "mx_linear_batched")
+    return outs
 
 
 def dequantize(q: QTensor, out=None, stream=None):

@@ -275,8 +275,12 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
   return hip_status(mx::quantize_dual_launch(a, static_cast<hipStream_t>(stream)));
 }
 
-mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C, int64_t ldc,
-                    int32_t out_dtype, void *stream) {
+namespace {
+
+// mx_linear's checks of one (A, B, C) entry; fills the GEMM's extents and the
+// entry's pointers. *empty is set when M or N is 0 (nothing to launch).
+mx_status linear_entry(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C, int64_t ldc,
+                       int32_t out_dtype, mx::GemmArgs *g, bool *empty) {
   if (op != MX_OP_FPROP && op != MX_OP_DGRAD && op != MX_OP_WGRAD) return MX_ERR_ARG;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_ARG;
   mx_status st = check_qtensor(A);
@@ -295,23 +299,59 @@ mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *
   operand_extents(B, &N, &Kb);
   if (Ka != Kb) return MX_ERR_SHAPE;
   if (ldc < N) return MX_ERR_SHAPE;
-  if (M == 0 || N == 0) return MX_OK;
-  if (C == nullptr) return MX_ERR_NULL;
-  if (!aligned(C, out_dtype == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
+  *empty = M == 0 || N == 0;
+  if (!*empty) {
+    if (C == nullptr) return MX_ERR_NULL;
+    if (!aligned(C, out_dtype == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
+  }
+  g->a_codes = static_cast<const uint8_t *>(A->codes);
+  g->a_scales = static_cast<const uint8_t *>(A->scales);
+  g->b_codes = static_cast<const uint8_t *>(B->codes);
+  g->b_scales = static_cast<const uint8_t *>(B->scales);
+  g->c = C;
+  g->M = M;
+  g->N = N;
+  g->K = Ka;
+  g->ldc = ldc;
+  g->out_bf16 = out_dtype == MX_OUT_BF16 ? 1 : 0;
+  return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C, int64_t ldc,
+                    int32_t out_dtype, void *stream) {
   mx::GemmArgs g;
-  g.a_codes = static_cast<const uint8_t *>(A->codes);
-  g.a_scales = static_cast<const uint8_t *>(A->scales);
-  g.b_codes = static_cast<const uint8_t *>(B->codes);
-  g.b_scales = static_cast<const uint8_t *>(B->scales);
-  g.c = C;
-  g.M = M;
-  g.N = N;
-  g.K = Ka;
-  g.ldc = ldc;
-  g.out_bf16 = out_dtype == MX_OUT_BF16 ? 1 : 0;
+  bool empty = false;
+  const mx_status st = linear_entry(op, A, B, C, ldc, out_dtype, &g, &empty);
+  if (st != MX_OK || empty) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(A->format == MX_FMT_FP8_E4M3 ? mx::gemm_e4m3_launch(g, s)
                                                  : mx::gemm_launch(g, s));
+}
+
+mx_status mx_linear_batched(int32_t op, int32_t count, const mx_qtensor *A, const mx_qtensor *B,
+                            void *const *C, int64_t ldc, int32_t out_dtype, void *stream) {
+  if (count < 1 || count > mx::kMaxGemmBatch) return MX_ERR_ARG;
+  if (A == nullptr || B == nullptr || C == nullptr) return MX_ERR_NULL;
+  mx::GemmArgs g;
+  bool empty = false;
+  for (int32_t i = 0; i < count; ++i) {
+    if (A[i].rows != A[0].rows || A[i].cols != A[0].cols || A[i].axis != A[0].axis ||
+        B[i].rows != B[0].rows || B[i].cols != B[0].cols || B[i].axis != B[0].axis)
+      return MX_ERR_SHAPE;
+    mx::GemmArgs gi;
+    const mx_status st = linear_entry(op, &A[i], &B[i], C[i], ldc, out_dtype, &gi, &empty);
+    if (st != MX_OK) return st;
+    if (A[i].format != MX_FMT_FP4_E2M1) return MX_ERR_UNSUPPORTED;
+    if (i == 0)
+      g = gi;
+    else
+      g.more[i - 1] = mx::GemmEntry{gi.a_codes, gi.a_scales, gi.b_codes, gi.b_scales, gi.c};
+  }
+  if (empty) return MX_OK;
+  g.batch = count;
+  return hip_status(mx::gemm_launch(g, static_cast<hipStream_t>(stream)));
 }
 
 mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *stream) {

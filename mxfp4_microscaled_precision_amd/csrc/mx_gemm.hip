@@ -46,6 +46,35 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, v4f c, u
                                                           (int)sa, SELB, (int)sb);
 }
 
+// Entry e of a grouped launch (e is wave-uniform: scalar selects, so the
+// kernel argument block is never indexed at run time).
+__device__ __forceinline__ GemmEntry entry_of(const GemmArgs &g, int e) {
+  GemmEntry p{g.a_codes, g.a_scales, g.b_codes, g.b_scales, g.c};
+#pragma unroll
+  for (int i = 1; i < kMaxGemmBatch; ++i)
+    if (e == i) p = g.more[i - 1];
+  return p;
+}
+
+// A buffer resource the compiler can keep in scalar registers (the value is
+// wave-uniform; the direct-to-LDS load takes it as an SGPR quad).
+__device__ __forceinline__ v4i uniform(v4i r) {
+  return v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+             __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
+// Tile t of the launch's (tall, for a grouped launch) tile grid -> entry and
+// the tile's coordinates within that entry's output. tm = tile rows per entry.
+__device__ __forceinline__ void tile_of(const GemmArgs &g, int t, int tm, int tn, int *e, int *mi,
+                                        int *ni) {
+  tile_coords(t, tm * g.batch, tn, mi, ni);
+  *e = 0;
+  if (g.batch > 1) {
+    *e = *mi / tm;
+    *mi -= *e * tm;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 256x256 block tile. Twelve waves, three per SIMD: eight consumer waves in
 // a 2x4 grid, 128x64 each = 8x4 MFMA tiles (128 fp32 accumulators per lane),
@@ -114,6 +143,18 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>,
   (consume_row<LO + I, S, ROWS>(acc, bf, af, a_base, sb, sa), ...);
 }
 
+// Whole 16-byte stores of output rows: C and its row pitch 16-byte aligned.
+template <int OUT_BF16>
+__device__ __forceinline__ bool c_line_ok(const GemmArgs &g) {
+  return ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
+}
+
+// One 8-byte (bf16) or 16-byte (fp32) store per quad.
+template <int OUT_BF16>
+__device__ __forceinline__ bool c_vec_ok(const GemmArgs &g) {
+  return ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) && ((g.ldc & 3) == 0);
+}
+
 // The consumers' stage loop. The consumers of wave row 0 wait at the barrier
 // that publishes stage G, then read its first fragments. Those of wave row 1
 // (SHIFTED; waves 4..7, so each SIMD holds one of each kind) run most of a
@@ -170,21 +211,28 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
     }
     if (++cs == nslices) {
       cs = 0;
-      int mi, ni;
-      tile_coords(g.tile_base + (kHalf ? (bid >> 1) : bid + ck * grid), tm, tn, &mi, &ni);
+      int e, mi, ni;
+      tile_of(g, g.tile_base + (kHalf ? (bid >> 1) : bid + ck * grid), tm, tn, &e, &mi, &ni);
       ++ck;
       // a half tile is rows 128 (bid & 1) .. + 127 of the 256-row tile
       const int64_t rbase = (int64_t)mi * kBM + (kHalf ? (bid & 1) * 128 : 0) + wm * (ROWS * 16);
       const int64_t cbase = (int64_t)ni * kBN + wn * 64;
-      if (line_ok && rbase + ROWS * 16 <= g.M && cbase + 64 <= g.N) {
-        store_tile_lds<OUT_BF16, ROWS>(g, acc, slab, rbase, cbase, lr, lg);
+      GemmArgs ge = g;
+      bool lok = line_ok, vok = vec_ok;
+      if (g.batch > 1) {
+        ge.c = entry_of(g, e).c;
+        lok = c_line_ok<OUT_BF16>(ge);
+        vok = c_vec_ok<OUT_BF16>(ge);
+      }
+      if (lok && rbase + ROWS * 16 <= g.M && cbase + 64 <= g.N) {
+        store_tile_lds<OUT_BF16, ROWS>(ge, acc, slab, rbase, cbase, lr, lg);
       } else {
         const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
 #pragma unroll
         for (int i = 0; i < ROWS; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
+            store_quad_vec<OUT_BF16>(ge, acc[i][j], row0 + i * 16, col0 + j * 16, vok);
       }
 #pragma unroll
       for (int i = 0; i < ROWS; ++i)
@@ -235,10 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
-    const v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
-    const v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
-    const v4i rsrc_s = p == 0 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
-                              : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+    v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
+    v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
+    v4i rsrc_s = p == 0 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
+                        : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
     const int s_panels = (p == 0 ? mp : np) >> 8;              // 256-row panels
     const int s_bytes = p == 0 ? sa_bytes : sb_bytes;
     const int s_lane = lane * 16;
@@ -246,8 +294,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     bool tile_live = false;
     auto set_tile = [&](int k) {
       tile_live = k < ntl;
-      int mi = 0, ni = 0;
-      if (tile_live) tile_coords(g.tile_base + (HALF ? (bid >> 1) : bid + k * grid), tm, tn, &mi, &ni);
+      int e = 0, mi = 0, ni = 0;
+      if (tile_live) tile_of(g, g.tile_base + (HALF ? (bid >> 1) : bid + k * grid), tm, tn, &e, &mi, &ni);
+      if (g.batch > 1 && tile_live) {                          // this tile's entry
+        const GemmEntry en = entry_of(g, e);
+        rsrc_a = uniform(make_rsrc(en.a_codes, (uint32_t)a_bytes));
+        rsrc_b = uniform(make_rsrc(en.b_codes, (uint32_t)b_bytes));
+        rsrc_s = uniform(p == 0 ? make_rsrc(en.a_scales, (uint32_t)sa_bytes)
+                                : make_rsrc(en.b_scales, (uint32_t)sb_bytes));
+      }
       ga = mi * (kBM / 16) + (HALF ? half * 8 + p * 2 : p * 4);
       gb = ni * (kBN / 16) + p * 4;
       gs = p == 0 ? mi : ni;                                   // the tile's panel
@@ -303,11 +358,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   }
 
   // consumers
-  // whole 16-byte stores: C and its row pitch 16-byte aligned
-  const bool line_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) &&
-                       ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) &&
-                      ((g.ldc & 3) == 0);
+  const bool line_ok = c_line_ok<OUT_BF16>(g);
+  const bool vec_ok = c_vec_ok<OUT_BF16>(g);
   constexpr int kRows = HALF ? 4 : 8;                          // MFMA rows per consumer
   const uint32_t a_off = (uint32_t)((wm * kRows) * 1024 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
@@ -358,13 +410,21 @@ int cu_count() {
 }
 
 hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
+  if (g.batch < 1 || g.batch > kMaxGemmBatch) return hipErrorInvalidValue;
   if (g.K == 0) {
     const int64_t total = g.M * g.N;
     const dim3 grid((unsigned)((total + 255) / 256));
-    return g.out_bf16 ? launch(fill_zero_kernel<1>, grid, dim3(256), 0, stream, g)
-                      : launch(fill_zero_kernel<0>, grid, dim3(256), 0, stream, g);
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < g.batch && e == hipSuccess; ++i) {
+      GemmArgs z = g;
+      if (i > 0) z.c = g.more[i - 1].c;
+      e = g.out_bf16 ? launch(fill_zero_kernel<1>, grid, dim3(256), 0, stream, z)
+                     : launch(fill_zero_kernel<0>, grid, dim3(256), 0, stream, z);
+    }
+    return e;
   }
-  const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
+  // a grouped launch stacks the entries' tile rows into one tall grid
+  const int64_t tiles = ((g.M + kBM - 1) / kBM) * g.batch * ((g.N + kBN - 1) / kBN);
   const int64_t cus = cu_count();
   // When the last round of whole tiles would fill at most half the compute
   // units (e.g. 896 tiles = 3.5 rounds on 256, or 64 tiles in all), the

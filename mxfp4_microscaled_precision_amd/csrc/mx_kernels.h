@@ -60,6 +60,15 @@ struct DualArgs {
 
 hipError_t quantize_dual_launch(const DualArgs &a, hipStream_t stream);
 
+// Operands and output of one GEMM of a grouped launch.
+struct GemmEntry {
+  const uint8_t *a_codes, *a_scales;
+  const uint8_t *b_codes, *b_scales;
+  void *c;
+};
+
+constexpr int kMaxGemmBatch = 4;
+
 struct GemmArgs {
   const uint8_t *a_codes, *a_scales;  // [M][K/2], [M][K/32]
   const uint8_t *b_codes, *b_scales;  // [N][K/2], [N][K/32]
@@ -69,6 +78,11 @@ struct GemmArgs {
   // Set by the launcher: the output tiles (in its ordering) one launch of
   // the MXFP4 GEMM covers, [tile_base, tile_base + tile_count).
   int tile_base, tile_count;
+  // Grouped launch (MXFP4 only): `batch` GEMMs of this one shape, entry 0 in
+  // the fields above and entry e > 0 in more[e - 1]. Their tile rows are
+  // stacked into one tall grid: tile row i of entry e is row e * tiles_m + i.
+  int batch = 1;
+  GemmEntry more[kMaxGemmBatch - 1] = {};
 };
 
 hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream);

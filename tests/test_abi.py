@@ -254,6 +254,39 @@ def test_linear_empty_is_a_noop():
     assert _lin(lib, 2, _desc(64, 0, 0), _desc(64, 32, 0), C=None) == 0
 
 
+def _linb(lib, op, As, Bs, Cs=None, ldc=None, out=0, count=None):
+    n = len(As)
+    da = (mx.QTensorDesc * n)(*As)
+    db = (mx.QTensorDesc * n)(*Bs)
+    Cs = [4096 * (i + 1) for i in range(n)] if Cs is None else Cs
+    cs = (ctypes.c_void_p * n)(*Cs)
+    ldc = ldc if ldc is not None else (Bs[0].rows if Bs[0].axis == 1 else Bs[0].cols)
+    return lib.mx_linear_batched(op, n if count is None else count, da, db, cs, ldc, out, None)
+
+
+def test_linear_batched_rejects_before_launch():
+    """Validation of mx_linear_batched fails before any HIP call; every entry
+    is checked as mx_linear checks it."""
+    lib = mx.load_library()
+    X, W = _desc(64, 128, 1), _desc(96, 128, 1)
+    assert _linb(lib, 0, [X, X], [W, W], count=0) == -4
+    assert _linb(lib, 0, [X] * 4, [W] * 4, count=5) == -4
+    assert lib.mx_linear_batched(0, 1, None, None, None, 96, 0, None) == -1
+    assert _linb(lib, 0, [X, _desc(32, 128, 1)], [W, W]) == -2           # entry rows differ
+    assert _linb(lib, 0, [X, X], [W, _desc(64, 128, 1)]) == -2           # entry N differs
+    assert _linb(lib, 0, [X, X], [W, _desc(96, 160, 1)]) == -2           # entry K differs
+    assert _linb(lib, 0, [X, X], [W, _desc(96, 128, 1, rot=0)]) == -5    # second pair's rotations
+    assert _linb(lib, 1, [X, X], [W, W]) == -4                           # dgrad needs B on axis 0
+    assert _linb(lib, 0, [X, X], [W, W], Cs=[4096, None]) == -1
+    assert _linb(lib, 0, [X, X], [W, W], Cs=[4096, 4098]) == -3          # fp32 C misaligned
+    assert _linb(lib, 0, [X, X], [W, W], ldc=95) == -2
+    assert _linb(lib, 0, [X, X], [W, W], out=2) == -4
+    E = _desc(64, 128, 1, fmt=1)
+    assert _linb(lib, 0, [E, E], [_desc(96, 128, 1, fmt=1)] * 2, Cs=[4096, 8192]) == -6  # MXFP8
+    # empty problem: nothing launched
+    assert _linb(lib, 0, [_desc(0, 128, 1)] * 2, [W, W], Cs=[None, None]) == 0
+
+
 def test_dequantize_rejects_before_launch():
     lib = mx.load_library()
     deq = lambda d, out=4096, ld=None: lib.mx_dequantize(  # noqa: E731

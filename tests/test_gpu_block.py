@@ -135,3 +135,38 @@ def test_block_linear(mx, li, variant):
         torch.cuda.synchronize()
     del q, dev
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pair", [("k_proj", "v_proj"), ("gate_proj", "up_proj")],
+                         ids=["k_v", "gate_up"])
+def test_block_grouped_gemms_equal_single(mx, pair):
+    """The benchmark step runs k/v and gate/up as one grouped launch per op
+    (mx_linear_batched). At full size, under the deterministic H32 variant,
+    every grouped output equals the single launch's bit for bit; the single
+    launches are the ones test_block_linear checks against the oracle."""
+    import torch
+    print(f"[block] grouped {pair}", flush=True)
+    names = [lin.name for lin in LLAMA_BLOCK_LINEARS]
+    _, rot, rnd, seed = VARIANTS[0]
+    sa = seed & 0xFFFFFFFF
+    sb = sa | (1 << 32)
+    seeds = {"X": (sa, sb), "W": (sb, sb), "dY": (sa, sa)}
+    q = []
+    for name in pair:
+        host = _tensors(names.index(name))
+        qq = {}
+        for k in ("X", "W", "dY"):
+            q1, q0 = mx.quantize_dual(to_dev(host[k]), rot, rnd, seed1=seeds[k][0],
+                                      seed0=seeds[k][1])
+            qq[k, 1], qq[k, 0] = q1, q0
+        q.append(qq)
+    for op, a, b, odt in OPS:
+        got = mx.linear_batched(op, [qq[a] for qq in q], [qq[b] for qq in q], odt)
+        for i, qq in enumerate(q):
+            ref = mx.linear(op, qq[a], qq[b], odt)
+            torch.cuda.synchronize()
+            assert torch.equal(got[i], ref), f"{pair[i]} {op}: grouped != single launch"
+            del ref
+        del got
+    del q
+    torch.cuda.empty_cache()
