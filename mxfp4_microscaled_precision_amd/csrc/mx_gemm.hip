@@ -46,15 +46,18 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4 &a, const uint4 &b, v4f c, u
                                                           (int)sa, SELB, (int)sb);
 }
 
-// Entry e of a grouped launch (e is wave-uniform: scalar selects, so the
-// kernel argument block is never indexed at run time).
+// Entry e of a grouped launch, one field at a time (e is wave-uniform:
+// scalar selects between fields at fixed offsets, so the kernel argument
+// block is never indexed at run time, which would copy it to scratch).
+static_assert(kMaxGemmBatch == 4, "entry selects");
+#define MX_ENTRY_FIELD(g, e, f) \
+  ((e) == 1 ? (g).more[0].f : (e) == 2 ? (g).more[1].f : (e) == 3 ? (g).more[2].f : (g).f)
 __device__ __forceinline__ GemmEntry entry_of(const GemmArgs &g, int e) {
-  GemmEntry p{g.a_codes, g.a_scales, g.b_codes, g.b_scales, g.c};
-#pragma unroll
-  for (int i = 1; i < kMaxGemmBatch; ++i)
-    if (e == i) p = g.more[i - 1];
-  return p;
+  return GemmEntry{MX_ENTRY_FIELD(g, e, a_codes), MX_ENTRY_FIELD(g, e, a_scales),
+                   MX_ENTRY_FIELD(g, e, b_codes), MX_ENTRY_FIELD(g, e, b_scales),
+                   MX_ENTRY_FIELD(g, e, c)};
 }
+#undef MX_ENTRY_FIELD
 
 // A buffer resource the compiler can keep in scalar registers (the value is
 // wave-uniform; the direct-to-LDS load takes it as an SGPR quad).
@@ -65,11 +68,12 @@ __device__ __forceinline__ v4i uniform(v4i r) {
 
 // Tile t of the launch's (tall, for a grouped launch) tile grid -> entry and
 // the tile's coordinates within that entry's output. tm = tile rows per entry.
+template <bool BATCHED>
 __device__ __forceinline__ void tile_of(const GemmArgs &g, int t, int tm, int tn, int *e, int *mi,
                                         int *ni) {
-  tile_coords(t, tm * g.batch, tn, mi, ni);
+  tile_coords(t, BATCHED ? tm * g.batch : tm, tn, mi, ni);
   *e = 0;
-  if (g.batch > 1) {
+  if (BATCHED) {
     *e = *mi / tm;
     *mi -= *e * tm;
   }
@@ -145,14 +149,14 @@ __device__ __forceinline__ void consume_rows(std::integer_sequence<int, I...>,
 
 // Whole 16-byte stores of output rows: C and its row pitch 16-byte aligned.
 template <int OUT_BF16>
-__device__ __forceinline__ bool c_line_ok(const GemmArgs &g) {
-  return ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((g.ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
+__device__ __forceinline__ bool c_line_ok(const void *c, int64_t ldc) {
+  return ((reinterpret_cast<uintptr_t>(c) & 15) == 0) && ((ldc * (OUT_BF16 ? 2 : 4)) & 15) == 0;
 }
 
 // One 8-byte (bf16) or 16-byte (fp32) store per quad.
 template <int OUT_BF16>
-__device__ __forceinline__ bool c_vec_ok(const GemmArgs &g) {
-  return ((reinterpret_cast<uintptr_t>(g.c) & (OUT_BF16 ? 7 : 15)) == 0) && ((g.ldc & 3) == 0);
+__device__ __forceinline__ bool c_vec_ok(const void *c, int64_t ldc) {
+  return ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0) && ((ldc & 3) == 0);
 }
 
 // The consumers' stage loop. The consumers of wave row 0 wait at the barrier
@@ -169,7 +173,7 @@ __device__ __forceinline__ bool c_vec_ok(const GemmArgs &g) {
 // barriers. Measured against all consumers waiting at every barrier: 3-5%
 // faster on Fprop, Dgrad and Wgrad; splitting after 5 or 4 rows (more
 // fragments live across the barrier) was slower.
-template <int OUT_BF16, bool SHIFTED, int ROWS>
+template <int OUT_BF16, bool SHIFTED, int ROWS, bool BATCHED>
 __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, int total,
                                               int nslices, int bid, int grid, int tm, int tn,
                                               bool vec_ok, bool line_ok, uint32_t a_off,
@@ -212,27 +216,28 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
     if (++cs == nslices) {
       cs = 0;
       int e, mi, ni;
-      tile_of(g, g.tile_base + (kHalf ? (bid >> 1) : bid + ck * grid), tm, tn, &e, &mi, &ni);
+      tile_of<BATCHED>(g, g.tile_base + (kHalf ? (bid >> 1) : bid + ck * grid), tm, tn, &e, &mi,
+                       &ni);
       ++ck;
       // a half tile is rows 128 (bid & 1) .. + 127 of the 256-row tile
       const int64_t rbase = (int64_t)mi * kBM + (kHalf ? (bid & 1) * 128 : 0) + wm * (ROWS * 16);
       const int64_t cbase = (int64_t)ni * kBN + wn * 64;
-      GemmArgs ge = g;
+      void *c = g.c;
       bool lok = line_ok, vok = vec_ok;
-      if (g.batch > 1) {
-        ge.c = entry_of(g, e).c;
-        lok = c_line_ok<OUT_BF16>(ge);
-        vok = c_vec_ok<OUT_BF16>(ge);
+      if (BATCHED) {
+        c = entry_of(g, e).c;
+        lok = c_line_ok<OUT_BF16>(c, g.ldc);
+        vok = c_vec_ok<OUT_BF16>(c, g.ldc);
       }
       if (lok && rbase + ROWS * 16 <= g.M && cbase + 64 <= g.N) {
-        store_tile_lds<OUT_BF16, ROWS>(ge, acc, slab, rbase, cbase, lr, lg);
+        store_tile_lds<OUT_BF16, ROWS>(g, c, acc, slab, rbase, cbase, lr, lg);
       } else {
         const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
 #pragma unroll
         for (int i = 0; i < ROWS; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            store_quad_vec<OUT_BF16>(ge, acc[i][j], row0 + i * 16, col0 + j * 16, vok);
+            store_quad_vec<OUT_BF16>(g, c, acc[i][j], row0 + i * 16, col0 + j * 16, vok);
       }
 #pragma unroll
       for (int i = 0; i < ROWS; ++i)
@@ -254,7 +259,7 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
 // twelve waves: consumers on 64x64 pieces (4 rows of 4 MFMAs), producers
 // copying the half's 8 A row groups and all 16 of B. Each output element
 // sees the same MFMAs in the same order as in a whole tile.
-template <int OUT_BF16, int HALF>
+template <int OUT_BF16, int HALF, bool BATCHED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes + kConsumers * kSlab];
 
@@ -283,10 +288,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     const int p = wave - kConsumers;
     const int a_bytes = mp * nslices * 64, b_bytes = np * nslices * 64;
     const int sa_bytes = nslices * mp * 4, sb_bytes = nslices * np * 4;
-    v4i rsrc_a = make_rsrc(g.a_codes, (uint32_t)a_bytes);
-    v4i rsrc_b = make_rsrc(g.b_codes, (uint32_t)b_bytes);
-    v4i rsrc_s = p == 0 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
-                        : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+    const v4i rsrc_a0 = make_rsrc(g.a_codes, (uint32_t)a_bytes);
+    const v4i rsrc_b0 = make_rsrc(g.b_codes, (uint32_t)b_bytes);
+    const v4i rsrc_s0 = p == 0 ? make_rsrc(g.a_scales, (uint32_t)sa_bytes)
+                               : make_rsrc(g.b_scales, (uint32_t)sb_bytes);
+    // a grouped launch switches them to each tile's entry
+    v4i rsrc_a = rsrc_a0, rsrc_b = rsrc_b0, rsrc_s = rsrc_s0;
     const int s_panels = (p == 0 ? mp : np) >> 8;              // 256-row panels
     const int s_bytes = p == 0 ? sa_bytes : sb_bytes;
     const int s_lane = lane * 16;
@@ -295,8 +302,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     auto set_tile = [&](int k) {
       tile_live = k < ntl;
       int e = 0, mi = 0, ni = 0;
-      if (tile_live) tile_of(g, g.tile_base + (HALF ? (bid >> 1) : bid + k * grid), tm, tn, &e, &mi, &ni);
-      if (g.batch > 1 && tile_live) {                          // this tile's entry
+      if (tile_live)
+        tile_of<BATCHED>(g, g.tile_base + (HALF ? (bid >> 1) : bid + k * grid), tm, tn, &e, &mi,
+                         &ni);
+      if (BATCHED && tile_live) {                              // this tile's entry
         const GemmEntry en = entry_of(g, e);
         rsrc_a = uniform(make_rsrc(en.a_codes, (uint32_t)a_bytes));
         rsrc_b = uniform(make_rsrc(en.b_codes, (uint32_t)b_bytes));
@@ -310,6 +319,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
     int ik = 0, is = 0;                                        // next stage to copy
     set_tile(0);
     auto issue = [&](int buf) {
+      // the copies take their buffer resources in scalar registers
+      const v4i ra = BATCHED ? uniform(rsrc_a) : rsrc_a0;
+      const v4i rb = BATCHED ? uniform(rsrc_b) : rsrc_b0;
+      const v4i rs = BATCHED ? uniform(rsrc_s) : rsrc_s0;
       const uint32_t stage = smem_base + (uint32_t)(buf * kStageBytes);
       int al = ga * nslices * 1024 + lane * 16, bl = gb * nslices * 1024 + lane * 16;
       int sl = s_lane + gs * 1024;
@@ -319,13 +332,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
         const int off = (j * nslices + is) * 1024;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 4 + j) * 1024));
         if (!HALF || j < 2)
-          dma_load16(rsrc_a, tile_live ? al + off : a_bytes,
+          dma_load16(ra, tile_live ? al + off : a_bytes,
                      HALF ? __builtin_amdgcn_readfirstlane(stage + (uint32_t)((p * 2 + j) * 1024))
                           : dst);
-        dma_load16(rsrc_b, tile_live ? bl + off : b_bytes, dst + kStageA);
+        dma_load16(rb, tile_live ? bl + off : b_bytes, dst + kStageA);
       }
       if (p < 2)
-        dma_load16(rsrc_s, tile_live ? sl + is * s_panels * 1024 : s_bytes,
+        dma_load16(rs, tile_live ? sl + is * s_panels * 1024 : s_bytes,
                    __builtin_amdgcn_readfirstlane(
                        stage + (uint32_t)(kStageA + kStageB + (p == 0 ? 0 : kStageSA))));
       if (++is == nslices) {
@@ -358,8 +371,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   }
 
   // consumers
-  const bool line_ok = c_line_ok<OUT_BF16>(g);
-  const bool vec_ok = c_vec_ok<OUT_BF16>(g);
+  const bool line_ok = c_line_ok<OUT_BF16>(g.c, g.ldc);
+  const bool vec_ok = c_vec_ok<OUT_BF16>(g.c, g.ldc);
   constexpr int kRows = HALF ? 4 : 8;                          // MFMA rows per consumer
   const uint32_t a_off = (uint32_t)((wm * kRows) * 1024 + lane * 16);
   const uint32_t b_off = (uint32_t)(kStageA + (wn * 4) * 1024 + lane * 16);
@@ -373,10 +386,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
                           (HALF ? (2 * half + wm) * 256 : wm * 512) + lane * 4;
   const uint32_t sb_off = (uint32_t)(kStageA + kStageB + kStageSA) + wn * 256 + lane * 4;
   if (wm == 1)
-    consumer_loop<OUT_BF16, true, kRows>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
+    consumer_loop<OUT_BF16, true, kRows, BATCHED>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
                                          line_ok, a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
   else
-    consumer_loop<OUT_BF16, false, kRows>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
+    consumer_loop<OUT_BF16, false, kRows, BATCHED>(g, smem, total, nslices, bid, grid, tm, tn, vec_ok,
                                           line_ok, a_off, b_off, sa_off, sb_off, lr, lg, wm, wn);
 }
 
@@ -436,18 +449,23 @@ hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
   a.tile_base = 0;
   a.tile_count = (int)(split ? tiles - rem : tiles);
   hipError_t e = hipSuccess;
+  // single GEMMs keep an instance without the grouped launch's per-tile
+  // entry logic (measured 2-5% faster than sharing the grouped instance)
+  const bool b = g.batch > 1;
   if (a.tile_count > 0) {
     const dim3 grid((unsigned)std::min<int64_t>(a.tile_count, cus));
-    e = g.out_bf16 ? launch(gemm_tiled_kernel<1, 0>, grid, dim3(kThreads), 0, stream, a)
-                   : launch(gemm_tiled_kernel<0, 0>, grid, dim3(kThreads), 0, stream, a);
+    auto k = g.out_bf16 ? (b ? gemm_tiled_kernel<1, 0, true> : gemm_tiled_kernel<1, 0, false>)
+                        : (b ? gemm_tiled_kernel<0, 0, true> : gemm_tiled_kernel<0, 0, false>);
+    e = launch(k, grid, dim3(kThreads), 0, stream, a);
   }
   if (e != hipSuccess || !split) return e;
   GemmArgs h = g;
   h.tile_base = a.tile_count;
   h.tile_count = (int)rem;
   const dim3 hgrid((unsigned)(2 * rem));
-  return g.out_bf16 ? launch(gemm_tiled_kernel<1, 1>, hgrid, dim3(kThreads), 0, stream, h)
-                    : launch(gemm_tiled_kernel<0, 1>, hgrid, dim3(kThreads), 0, stream, h);
+  auto k = g.out_bf16 ? (b ? gemm_tiled_kernel<1, 1, true> : gemm_tiled_kernel<1, 1, false>)
+                      : (b ? gemm_tiled_kernel<0, 1, true> : gemm_tiled_kernel<0, 1, false>);
+  return launch(k, hgrid, dim3(kThreads), 0, stream, h);
 }
 
 }  // namespace mx

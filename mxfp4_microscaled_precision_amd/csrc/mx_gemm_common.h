@@ -41,17 +41,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Generic epilogue store of one quad: lane (lr, lg) of a 16x16 tile holds
 // C[row][col .. col + 3] with row = tile row + lr, col = tile col + 4 lg.
 // Element-wise and masked, for shapes the row-staged path does not take.
+// c is the output (g.c, or a grouped launch's entry's); g gives its extents
+// and row pitch.
 template <int OUT_BF16>
-__device__ __forceinline__ void store_quad(const GemmArgs &g, const v4f &acc, int64_t row,
+__device__ __forceinline__ void store_quad(const GemmArgs &g, void *c, const v4f &acc, int64_t row,
                                            int64_t col) {
   if (row >= g.M) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (col + r < g.N) {
       if (OUT_BF16)
-        reinterpret_cast<uint16_t *>(g.c)[row * g.ldc + col + r] = f32_to_bf16_rne(acc[r]);
+        reinterpret_cast<uint16_t *>(c)[row * g.ldc + col + r] = f32_to_bf16_rne(acc[r]);
       else
-        reinterpret_cast<float *>(g.c)[row * g.ldc + col + r] = acc[r];
+        reinterpret_cast<float *>(c)[row * g.ldc + col + r] = acc[r];
     }
   }
 }
@@ -104,21 +106,21 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int *mi, in
 // (B is the MFMA's first operand). One 8-byte (bf16) or 16-byte (fp32)
 // store when the address allows it, else element-wise.
 template <int OUT_BF16>
-__device__ __forceinline__ void store_quad_vec(const GemmArgs &g, const v4f &acc, int64_t row,
-                                               int64_t col, bool vec_ok) {
+__device__ __forceinline__ void store_quad_vec(const GemmArgs &g, void *c, const v4f &acc,
+                                               int64_t row, int64_t col, bool vec_ok) {
   if (row >= g.M) return;
   if (vec_ok && col + 3 < g.N) {
     if (OUT_BF16) {
       uint2 v;
       v.x = pack_bf16x2_rne(acc[0], acc[1]);
       v.y = pack_bf16x2_rne(acc[2], acc[3]);
-      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + row * g.ldc + col) = v;
+      *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(c) + row * g.ldc + col) = v;
     } else {
-      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + row * g.ldc + col) =
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(c) + row * g.ldc + col) =
           make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   } else {
-    store_quad<OUT_BF16>(g, acc, row, col);
+    store_quad<OUT_BF16>(g, c, acc, row, col);
   }
 }
 
@@ -137,9 +139,9 @@ constexpr int kSlab = 2048;                        // epilogue staging per 128x6
 // out) 228 -> 222 us. Wave tiles that cross the edge of C, or a C that is not
 // 16-byte aligned, keep the quad stores.
 template <int OUT_BF16, int ROWS>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&acc)[ROWS][4],
-                                               uint8_t *slab, int64_t row0, int64_t col0, int lr,
-                                               int lg) {
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &g, void *c,
+                                               const v4f (&acc)[ROWS][4], uint8_t *slab,
+                                               int64_t row0, int64_t col0, int lr, int lg) {
   // Opaque copies: keeps the compiler from hoisting these lane addresses
   // out of the stage loop, where they would hold registers the MFMA loop
   // needs.
@@ -150,7 +152,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &g, const v4f (&ac
   // 8 rows add `step`, the fp32 halves add 128 bytes (an immediate offset)
   constexpr int kEsize = OUT_BF16 ? 2 : 4;
   const int64_t step = 8 * g.ldc * kEsize;
-  uint8_t *pi = reinterpret_cast<uint8_t *>(g.c) + ((row0 + rr) * g.ldc + col0) * kEsize + ch * 16;
+  uint8_t *pi = reinterpret_cast<uint8_t *>(c) + ((row0 + rr) * g.ldc + col0) * kEsize + ch * 16;
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) {
 #pragma unroll

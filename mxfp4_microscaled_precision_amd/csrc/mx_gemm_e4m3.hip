@@ -212,14 +212,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_e4m3_kernel(GemmArgs g) {
       ++ck;
       const int64_t rbase = (int64_t)mi * kBM + wm * 128, cbase = (int64_t)ni * kBN + wn * 64;
       if (line_ok && rbase + 128 <= g.M && cbase + 64 <= g.N) {
-        store_tile_lds<OUT_BF16, 8>(g, acc, slab, rbase, cbase, lr, lg);
+        store_tile_lds<OUT_BF16, 8>(g, g.c, acc, slab, rbase, cbase, lr, lg);
       } else {
         const int64_t row0 = rbase + lr, col0 = cbase + 4 * lg;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            store_quad_vec<OUT_BF16>(g, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
+            store_quad_vec<OUT_BF16>(g, g.c, acc[i][j], row0 + i * 16, col0 + j * 16, vec_ok);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
