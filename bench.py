@@ -727,8 +727,9 @@ def main():
             },
             "pct_mfma_peak": round(100.0 * h["tflops"] / PEAK_FP4_TFLOPS, 2),
             "roofline": {
-                "kernel": "gemm_tiled_kernel<1, 0> (MXFP4 GEMM, bf16 out: the 14 Fprop and "
-                          "Dgrad GEMMs of a step, in 10 launches with k/v and gate/up grouped)",
+                "kernel": "gemm_tiled_kernel<1, 0, false|true> (MXFP4 GEMM, bf16 out: the 14 "
+                          "Fprop and Dgrad GEMMs of a step in 10 launches, 6 single and 4 "
+                          "grouped: k+v, gate+up)",
                 "bound": "mfma",
                 "achieved": round(dom_ach, 2),
                 "peak": PEAK_FP4_TFLOPS,
