@@ -259,6 +259,10 @@ __device__ __forceinline__ void consumer_loop(const GemmArgs &g, uint8_t *smem, 
 // twelve waves: consumers on 64x64 pieces (4 rows of 4 MFMAs), producers
 // copying the half's 8 A row groups and all 16 of B. Each output element
 // sees the same MFMAs in the same order as in a whole tile.
+//
+// BATCHED: a grouped launch (GemmArgs::batch entries of one shape, their tile
+// rows stacked into one grid); each tile takes its entry's operands and
+// output. Single GEMMs use the instances without it.
 template <int OUT_BF16, int HALF, bool BATCHED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStageBytes + kConsumers * kSlab];
