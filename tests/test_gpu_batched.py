@@ -107,3 +107,31 @@ def test_batched_strided_outputs_and_empty_k(mx):
     mx.linear_batched("fprop", za, zb, "f32", outs=outs)
     torch.cuda.synchronize()
     assert all(torch.all(o == 0.0) for o in outs), "K = 0 must write zeros"
+
+
+def test_batched_entries_with_different_quantizations(mx):
+    """Each entry keeps its own operands' quantization: entries quantized
+    with different rotations and roundings (each pair consistent) give the
+    single launches' outputs bit for bit, and the SR entry matches the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(515)
+    M, N, K = 384, 320, 256
+    variants = [("hadamard", "rne", 3), ("none", "sr", 9), ("rand_sign_hadamard", "rne", 11),
+                ("hadamard16", "sr", 4)]
+    qa, qb, srcs = [], [], []
+    for rot, rnd, seed in variants:
+        a, b = _sources("wgrad", M, N, K, rng)
+        srcs.append((a, b))
+        qa.append(mx.quantize(to_dev(a), 0, rot, rnd, seed=seed))
+        qb.append(mx.quantize(to_dev(b), 0, rot, rnd, seed=seed | (1 << 32)))
+    got = mx.linear_batched("wgrad", qa, qb, "f32")
+    torch.cuda.synchronize()
+    for i in range(len(variants)):
+        ref = mx.linear("wgrad", qa[i], qb[i], "f32")
+        torch.cuda.synchronize()
+        assert torch.equal(got[i], ref), f"entry {i} {variants[i]}: grouped != single launch"
+    a, b = srcs[1]
+    C_ref, _, _ = oracle.linear_ref("wgrad", a, b, rotate="none", rounding="sr", seed=9)
+    err = rel_fro(got[1].cpu().numpy(), C_ref)
+    assert err <= GEMM_TOL, f"SR entry: rel Frobenius {err:.3e}"
