@@ -717,8 +717,11 @@ __global__ __launch_bounds__(256) void quant_axis0_sr_kernel(
 // Workgroups past the last source row only write the axis-0 operand's K
 // padding (encoded zeros).
 // ---------------------------------------------------------------------------
+// At most 64 registers (8 waves per SIMD): the nearest-rounding instances
+// need 42-53 anyway; the stochastic-rounding ones, at 59-75 unbounded, ran
+// 0.5-3% faster bounded (one or two registers spilled; bitwise identical).
 template <int ROT, int RND>
-__global__ __launch_bounds__(256) void quant_dual_kernel(
+__global__ __launch_bounds__(256, 8) void quant_dual_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes1, uint8_t *__restrict__ scales1, uint32_t s1_lo, uint32_t s1_hi,
     uint8_t *__restrict__ codes0, uint8_t *__restrict__ scales0, uint32_t s0_lo, uint32_t s0_hi,
