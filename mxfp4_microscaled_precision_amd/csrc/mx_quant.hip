@@ -33,6 +33,7 @@ namespace mx {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Unnormalised butterfly: h = H32 x in fp32, strides 1, 2, 4, 8, 16, lower
 // index a + b, upper a - b. The normalisation y = fl32(h * c) is folded into
@@ -709,8 +710,11 @@ __global__ __launch_bounds__(256) void quant_axis0_sr_kernel(
 
 // ---------------------------------------------------------------------------
 // Both orientations from one read. A workgroup stages a 32-row x 128-column
-// piece of the source in LDS (chunk ch of row r at r * 256 + (ch ^ r) * 16,
-// r taken mod 16); threads 0..127 then encode its 128 row blocks into the
+// piece of the source in LDS, widened to fp32 (row stride 132 floats: one
+// 16-byte chunk of padding, so that the staging writes, the row reads and
+// the column reads below all spread over distinct banks, and every LDS
+// access is a base address plus immediate offsets); threads 0..127 then
+// encode its 128 row blocks into the
 // axis-1 operand (source rows, K along the columns) and threads 128..255 its
 // 128 column blocks into the axis-0 operand (source columns, K along the
 // rows), each exactly as quant_axis1_kernel / quant_axis0_kernel would.
@@ -718,15 +722,15 @@ __global__ __launch_bounds__(256) void quant_axis0_sr_kernel(
 // padding (encoded zeros).
 // ---------------------------------------------------------------------------
 // At most 64 registers (8 waves per SIMD): the nearest-rounding instances
-// need 42-53 anyway; the stochastic-rounding ones, at 59-75 unbounded, ran
-// 0.5-3% faster bounded (one or two registers spilled; bitwise identical).
+// need 48 anyway; the stochastic-rounding ones, at 59-75 unbounded, ran
+// 0.5-3% faster bounded (a few registers spilled; bitwise identical).
 template <int ROT, int RND>
 __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes1, uint8_t *__restrict__ scales1, uint32_t s1_lo, uint32_t s1_hi,
     uint8_t *__restrict__ codes0, uint8_t *__restrict__ scales0, uint32_t s0_lo, uint32_t s0_hi,
     int64_t gx) {
-  __shared__ __attribute__((aligned(16))) uint8_t st[32 * 256];
+  __shared__ __attribute__((aligned(16))) float st[32 * 132];
   const int tid = threadIdx.x;
   const int64_t bx = (int64_t)blockIdx.x % gx, by = (int64_t)blockIdx.x / gx;
   const int64_t C0 = bx * 128, R0 = by * 32;
@@ -736,16 +740,28 @@ __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
   const bool rows_live = R0 < rows;
 
   if (rows_live) {
-    const int ch = tid & 15;
-    const int64_t c = C0 + ch * 8;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rr = (tid >> 4) + 16 * j;
-      const u32x4 v = c < cols ? __builtin_nontemporal_load(
-                                     reinterpret_cast<const u32x4 *>(x + (R0 + rr) * ld + c))
-                               : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(st + rr * 256 + ((ch ^ (rr & 15)) << 4)) = v;
+    // lane (r0, q) loads columns 4q .. 4q + 3 and 64 + 4q .. 64 + 4q + 3 of
+    // rows r0 and r0 + 16, 8 bytes each and all four in flight at once (a
+    // wait between them cost 5-12%), and writes them widened. cols % 32 == 0:
+    // a group of four columns is all inside or all padding (zeros).
+    const int q = tid & 15, r0 = tid >> 4;
+    const int64_t c = C0 + 4 * q;
+    u32x2 v[4] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+    const uint16_t *p = x + R0 * ld + c + (int64_t)r0 * ld;
+    if (c < cols) {
+      v[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+      v[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + 16 * ld));
     }
+    if (c + 64 < cols) {
+      v[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + 64));
+      v[3] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + 16 * ld + 64));
+    }
+    float *d = st + r0 * 132 + 4 * q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4 *>(d + (k >> 1) * 16 * 132 + (k & 1) * 64) =
+          make_float4(bits_f(v[k].x << 16), bits_f(v[k].x & 0xFFFF0000u),
+                      bits_f(v[k].y << 16), bits_f(v[k].y & 0xFFFF0000u));
   }
   __syncthreads();
 
@@ -770,13 +786,12 @@ __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
     }
     if (kb >= nsl1 * 4) return;                           // past the operand's K extent
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((b * 4 + j) ^ (rr & 15)) << 4));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        y[8 * j + 2 * t] = bits_f(d[t] << 16);
-        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float4 f = *reinterpret_cast<const float4 *>(st + rr * 132 + b * 32 + 4 * j);
+      y[4 * j] = f.x;
+      y[4 * j + 1] = f.y;
+      y[4 * j + 2] = f.z;
+      y[4 * j + 3] = f.w;
     }
     if (ROT == MX_K_ROT_RAND_SIGN) apply_sign_mask(y, mask);
     rotate_block<ROT>(y);
@@ -792,9 +807,19 @@ __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
       for (int j = 0; j < 4; ++j) out[j] = 0u;
       s = 0u;
     }
-    *reinterpret_cast<uint4 *>(codes1 + code_offset(r, kb, nsl1)) =
-        make_uint4(out[0], out[1], out[2], out[3]);
-    scales1[scale_offset(r, kb, mnp1)] = (uint8_t)s;
+    // code_offset(r, kb, nsl1) and scale_offset(r, kb, mnp1) split into a
+    // uniform part and a 32-bit lane part (R0 % 32 == 0, C0 % 128 == 0: row
+    // group R0 / 16 + rr / 16, one K slice C0 / 128 for the four blocks,
+    // scale group R0 / 256; codes < 1 GiB)
+    {
+      const int64_t cu = ((R0 >> 4) * nsl1 + (C0 >> 7)) * 1024;
+      const uint32_t cl = ((rr >> 4) ? (uint32_t)nsl1 * 1024u : 0u) + (uint32_t)(b * 256 + (rr & 15) * 16);
+      const int64_t hR = (R0 >> 4) & 15;                  // even: + rr / 16 carries into no other field
+      const int64_t su = ((C0 >> 7) * (mnp1 >> 8) + (R0 >> 8)) * 1024 + (hR >> 2) * 256 + (hR & 3);
+      const uint32_t sl = (uint32_t)(b * 64 + (rr & 15) * 4 + (rr >> 4));
+      *reinterpret_cast<uint4 *>(codes1 + cu + cl) = make_uint4(out[0], out[1], out[2], out[3]);
+      scales1[su + sl] = (uint8_t)s;
+    }
   } else {
     // axis 0: column C0 + cc, 32-block R0 / 32 along the rows
     const int cc = tid - 128;
@@ -808,11 +833,7 @@ __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
       mask = gather_sign_mask(sign_nibble((uint32_t)((R0 >> 2) + (lane & 7)), s0_lo), 0);
     if (rows_live && c < cols) {                          // uniform over each quad (cols % 32 == 0)
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint16_t bits =
-            *reinterpret_cast<const uint16_t *>(st + j * 256 + (((cc >> 3) ^ (j & 15)) << 4) + (cc & 7) * 2);
-        y[j] = bits_f((uint32_t)bits << 16);
-      }
+      for (int j = 0; j < 32; ++j) y[j] = st[j * 132 + cc];
       if (ROT == MX_K_ROT_RAND_SIGN) apply_sign_mask(y, mask);
       rotate_block<ROT>(y);
       if (RND == MX_K_ROUND_SR) {
@@ -863,9 +884,17 @@ __global__ __launch_bounds__(256, 8) void quant_dual_kernel(
       for (int j = 0; j < 4; ++j) out[j] = 0u;
       s = 0u;
     }
-    *reinterpret_cast<uint4 *>(codes0 + code_offset(c, kb, nsl0)) =
-        make_uint4(out[0], out[1], out[2], out[3]);
-    scales0[scale_offset(c, kb, mnp0)] = (uint8_t)s;
+    // code_offset(c, kb, nsl0) and scale_offset(c, kb, mnp0) split the same
+    // way (C0 % 128 == 0: row group C0 / 16 + cc / 16, scale group C0 / 256)
+    {
+      const int64_t cu = ((C0 >> 4) * nsl0 + (kb >> 2)) * 1024 + (kb & 3) * 256;
+      const uint32_t cl = (uint32_t)(cc >> 4) * ((uint32_t)nsl0 * 1024u) + (uint32_t)((cc & 15) * 16);
+      const int h = (int)((C0 >> 4) & 15) + (cc >> 4);  // 0 or 8, plus 0..7
+      const int64_t su = ((kb >> 2) * (mnp0 >> 8) + (C0 >> 8)) * 1024 + (kb & 3) * 64;
+      const uint32_t sl = (uint32_t)((h >> 2) * 256 + (cc & 15) * 4 + (h & 3));
+      *reinterpret_cast<uint4 *>(codes0 + cu + cl) = make_uint4(out[0], out[1], out[2], out[3]);
+      scales0[su + sl] = (uint8_t)s;
+    }
   }
 }
 
