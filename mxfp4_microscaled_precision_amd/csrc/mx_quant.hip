@@ -349,21 +349,26 @@ __device__ __forceinline__ int64_t scale_offset(int64_t mn, int64_t kb, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// axis = 1 (blocks run along a source row): a wave encodes one output tile
-// (16 rows x 128 K elements) at a time and walks the tiles wave_id,
-// wave_id + waves, ...; the next tile's loads are in flight while the current
-// one is encoded. The tile's 4 KB of bf16 is read with each load instruction
-// covering four whole 256-byte row pieces, staged in LDS, and lane l then
-// takes row (l & 15), block (l >> 4): 64 bytes in, 16 code bytes out at
-// tile + 16 l (the wave writes its 1 KB tile in one go). LDS holds row r's
-// 16-byte chunk ch at r * 256 + (ch ^ r) * 16, so both the staging writes
-// and the per-lane reads hit 16 distinct chunk positions per 16 lanes.
+// axis = 1 (blocks run along a source row): each wave encodes one output tile
+// (16 rows x 128 K elements), four tiles per workgroup, one launch covering
+// every tile. The tile's 4 KB of bf16 is read with each load instruction
+// covering four whole 256-byte row pieces (all four in flight at once),
+// staged in LDS, and lane l then takes row (l & 15), block (l >> 4): 64
+// bytes in, 16 code bytes out at tile + 16 l (the wave writes its 1 KB tile
+// in one go). LDS holds row r's 16-byte chunk ch at r * 256 + (ch ^ r) * 16,
+// so both the staging writes and the per-lane reads hit 16 distinct chunk
+// positions per 16 lanes.
+// At most 85 registers (6 waves per SIMD); the nearest-rounding instances
+// need 53-55, so up to 8 waves per SIMD cover each other's loads. This was
+// 3-9% faster than a persistent grid of 12 waves per compute unit that kept
+// the next tile's loads in flight in registers (88 registers), and 5-9%
+// faster with stochastic rounding than a bound of 8 waves (bitwise
+// identical).
 // ---------------------------------------------------------------------------
-constexpr int kAxis1WgPerCu = 3;   // 12 waves per compute unit (measured best of 2, 3, 4, 6, 8)
 
 // The second operand of a two-operand launch (PAIR): a source with the same
 // column count whose row groups follow the first operand's in one sequence
-// of tiles, so both are walked by one persistent grid.
+// of tiles.
 struct Axis1Second {
   const uint16_t *x;
   int64_t rows, ld;
@@ -372,7 +377,7 @@ struct Axis1Second {
 };
 
 template <int ROT, int RND, int FMT, bool PAIR>
-__global__ __launch_bounds__(256) void quant_axis1_kernel(
+__global__ __launch_bounds__(256, 6) void quant_axis1_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, uint32_t seed_lo,
     uint32_t seed_hi, Axis1Second sec) {
@@ -386,122 +391,99 @@ __global__ __launch_bounds__(256) void quant_axis1_kernel(
   const uint32_t nslices = (uint32_t)((cols + 127) >> 7);
   const uint32_t ntiles = (gsplit + (uint32_t)(mnp2 >> 4)) * nslices;
   const int wv = threadIdx.x >> 6;
-  const uint32_t stride = gridDim.x * 4u;
-  uint32_t tile = blockIdx.x * 4u + (uint32_t)wv;
+  const uint32_t tile = blockIdx.x * 4u + (uint32_t)wv;
   if (tile >= ntiles) return;
   const int lane = threadIdx.x & 63;
   uint8_t *st = stage[wv];
   const int ch = lane & 15;
-  // (row group, K slice) of this tile and of the next one; the stride's own
-  // split advances them without a division per tile
-  const uint32_t st_g = stride / nslices, st_q = stride - st_g * nslices;
-  uint32_t g = tile / nslices, q = tile - g * nslices;
-  auto advance = [&](uint32_t &tg, uint32_t &tq) {
-    tq += st_q;
-    tg += st_g;
-    if (tq >= nslices) {
-      tq -= nslices;
-      ++tg;
-    }
-  };
-  // staging loads of a tile: instruction j reads rows 4j .. 4j + 3, 16 lanes per row
-  u32x4 v[4];
-  auto load_tile = [&](uint32_t tg, uint32_t tq) {
-    const bool two = PAIR && tg >= gsplit;                  // the tile is the second operand's
+  const uint32_t g = tile / nslices, q = tile - g * nslices;   // (row group, K slice)
+  const bool two = PAIR && g >= gsplit;                         // the second operand's tile
+  const uint32_t gl = two ? g - gsplit : g;
+  {
+    // instruction j reads rows 4j .. 4j + 3, 16 lanes per row. Rows and
+    // columns past the source are read from its last row / last chunk: only
+    // padding blocks use them (cols % 32 == 0, so a 32-block is all inside or
+    // all padding) and those are written as zeros below. Unconditional loads
+    // keep all four in flight; with a branch around each, the compiler
+    // waited for the first two before issuing the other two.
     const uint16_t *xs = two ? sec.x : x;
     const int64_t rs = two ? sec.rows : rows, ls = two ? sec.ld : ld;
-    const uint32_t lg = two ? tg - gsplit : tg;
-    const int64_t k = (int64_t)tq * 128 + ch * 8;           // first element of the chunk
+    const int64_t k = min((int64_t)q * 128 + ch * 8, cols - 8);   // first element of the chunk
+    u32x4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
-      const int64_t r = (int64_t)lg * 16 + rr;
-      v[j] = (r < rs && k < cols)
-                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xs + r * ls + k))
-                 : u32x4{0u, 0u, 0u, 0u};
+      const int64_t r = min((int64_t)gl * 16 + rr, rs - 1);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xs + r * ls + k));
     }
-  };
-  load_tile(g, q);
-  uint32_t gn = g, qn = q;
-  advance(gn, qn);
-  for (; tile < ntiles; tile += stride) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = j * 4 + (lane >> 4);
       *reinterpret_cast<u32x4 *>(st + rr * 256 + ((ch ^ rr) << 4)) = v[j];
     }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int rr = lane & 15, cb = lane >> 4;
+  const uint32_t s_lo = two ? sec.seed_lo : seed_lo, s_hi = two ? sec.seed_hi : seed_hi;
+  const int64_t r = (int64_t)gl * 16 + rr;
+  const int64_t kb = (int64_t)q * 4 + cb;
+  const bool valid = r < (two ? sec.rows : rows) && (kb << 5) < cols;
+  float y[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((cb * 4 + j) ^ rr) << 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      y[8 * j + 2 * t] = bits_f(d[t] << 16);
+      y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
+    }
+  }
+  if (ROT == MX_K_ROT_RAND_SIGN) {
+    // the tile's 128 reduction indices need 32 Philox calls: lanes 0..31
+    // make one each, the sign bits meet in LDS as one nibble per call
+    uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
+    if (lane < 32) {
+      const U4 sw = sign_words((uint32_t)(q * 32 + lane), s_lo);
+      sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (tile + stride < ntiles) load_tile(gn, qn);          // next tile's loads in flight
-
-    const int rr = lane & 15, cb = lane >> 4;
-    const bool two = PAIR && g >= gsplit;                   // wave-uniform
-    const uint32_t gl = two ? g - gsplit : g;
-    const uint32_t s_lo = two ? sec.seed_lo : seed_lo, s_hi = two ? sec.seed_hi : seed_hi;
-    const int64_t r = (int64_t)gl * 16 + rr;
-    const int64_t kb = (int64_t)q * 4 + cb;
-    const bool valid = r < (two ? sec.rows : rows) && (kb << 5) < cols;
-    float y[32];
+    uint32_t mask = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 d = *reinterpret_cast<const u32x4 *>(st + rr * 256 + (((cb * 4 + j) ^ rr) << 4));
+    for (int j = 0; j < 8; ++j) mask |= sg[cb * 8 + j] << (4 * j);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        y[8 * j + 2 * t] = bits_f(d[t] << 16);
-        y[8 * j + 2 * t + 1] = bits_f(d[t] & 0xFFFF0000u);
-      }
-    }
-    if (ROT == MX_K_ROT_RAND_SIGN) {
-      // the tile's 128 reduction indices need 32 Philox calls: lanes 0..31
-      // make one each, the sign bits meet in LDS as one nibble per call
-      uint32_t *sg = reinterpret_cast<uint32_t *>(signs_lds[wv]);
-      if (lane < 32) {
-        const U4 sw = sign_words((uint32_t)(q * 32 + lane), s_lo);
-        sg[lane] = (sw.x >> 31) | ((sw.y >> 31) << 1) | ((sw.z >> 31) << 2) | ((sw.w >> 31) << 3);
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      uint32_t mask = 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mask |= sg[cb * 8 + j] << (4 * j);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
-    }
-    rotate_block<ROT>(y);
-    // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
-    const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
-    U4 w{0u, 0u, 0u, 0u};
-    auto u24_of = [&](int i) -> uint32_t {
-      if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), s_lo, s_hi);
-      return pick_word(w, (uint32_t)(i & 3)) >> 8;
-    };
-    constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
-    uint32_t out[kWords];
-    uint32_t s = quantize_block<RotKind<ROT>::value, RND, FMT>(y, out, u24_of);
-    if (!valid) {                                         // padding: zero codes, scale code 0
-#pragma unroll
-      for (int j = 0; j < kWords; ++j) out[j] = 0u;
-      s = 0u;
-    }
-    if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
-      uint8_t *tp = codes + (size_t)tile * 2048 + cb * 512 + rr * 16;
-      *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
-      *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
-    } else {
-      const uint32_t lt = PAIR ? gl * nslices + q : tile;   // tile within its operand
-      *reinterpret_cast<uint4 *>((two ? sec.codes : codes) + (size_t)lt * 1024 + lane * 16) =
-          make_uint4(out[0], out[1], out[2], out[3]);
-    }
-    (two ? sec.scales : scales)[scale_offset(r, kb, two ? mnp2 : mnp)] = (uint8_t)s;
-    g = gn;
-    q = qn;
-    advance(gn, qn);
-    __builtin_amdgcn_wave_barrier();        // all lanes done with st before it is rewritten
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = 0; i < 32; ++i) y[i] = bits_f(f_bits(y[i]) ^ ((mask << (31 - i)) & 0x80000000u));
   }
+  rotate_block<ROT>(y);
+  // stochastic rounding index L = r * cols + kb * 32 + i (cols % 32 == 0)
+  const uint64_t q0 = (uint64_t)(r * cols + (kb << 5)) >> 2;
+  U4 w{0u, 0u, 0u, 0u};
+  auto u24_of = [&](int i) -> uint32_t {
+    if ((i & 3) == 0) w = sr_words(q0 + (uint64_t)(i >> 2), s_lo, s_hi);
+    return pick_word(w, (uint32_t)(i & 3)) >> 8;
+  };
+  constexpr int kWords = FMT == kFmtE4M3 ? 8 : 4;
+  uint32_t out[kWords];
+  uint32_t s = quantize_block<RotKind<ROT>::value, RND, FMT>(y, out, u24_of);
+  if (!valid) {                                           // padding: zero codes, scale code 0
+#pragma unroll
+    for (int j = 0; j < kWords; ++j) out[j] = 0u;
+    s = 0u;
+  }
+  if constexpr (FMT == kFmtE4M3) {  // block cb of row rr: chunks 2 cb and 2 cb + 1
+    uint8_t *tp = codes + (size_t)tile * 2048 + cb * 512 + rr * 16;
+    *reinterpret_cast<uint4 *>(tp) = make_uint4(out[0], out[1], out[2], out[3]);
+    *reinterpret_cast<uint4 *>(tp + 256) = make_uint4(out[4], out[5], out[6], out[7]);
+  } else {
+    const uint32_t lt = PAIR ? gl * nslices + q : tile;     // tile within its operand
+    *reinterpret_cast<uint4 *>((two ? sec.codes : codes) + (size_t)lt * 1024 + lane * 16) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  (two ? sec.scales : scales)[scale_offset(r, kb, two ? mnp2 : mnp)] = (uint8_t)s;
 }
 
 // ---------------------------------------------------------------------------
@@ -915,7 +897,7 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   if (a.axis == 1) {
     const int64_t mnp = (a.rows + 255) & ~(int64_t)255;
     const int64_t ntiles = (mnp >> 4) * ((a.cols + 127) >> 7);
-    const int64_t blocks = std::min<int64_t>((ntiles + 3) / 4, (int64_t)cu_count() * kAxis1WgPerCu);
+    const int64_t blocks = (ntiles + 3) / 4;                  // one tile per wave
     return launch(quant_axis1_kernel<ROT, RND, FMT, false>, dim3((unsigned)blocks), dim3(256), 0,
                   stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi,
                   Axis1Second{});
@@ -949,7 +931,7 @@ template <int ROT, int RND>
 hipError_t launch_pair(const QuantArgs &a, const QuantArgs &b, hipStream_t stream) {
   const int64_t mnp = (a.rows + 255) & ~(int64_t)255, mnp2 = (b.rows + 255) & ~(int64_t)255;
   const int64_t ntiles = ((mnp + mnp2) >> 4) * ((a.cols + 127) >> 7);
-  const int64_t blocks = std::min<int64_t>((ntiles + 3) / 4, (int64_t)cu_count() * kAxis1WgPerCu);
+  const int64_t blocks = (ntiles + 3) / 4;                    // one tile per wave
   const Axis1Second sec{b.x, b.rows, b.ld, b.codes, b.scales, b.seed_lo, b.seed_hi};
   return launch(quant_axis1_kernel<ROT, RND, kFmtE2M1, true>, dim3((unsigned)blocks), dim3(256), 0,
                 stream, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.seed_lo, a.seed_hi, sec);
