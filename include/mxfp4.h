@@ -201,7 +201,7 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
  * Two axis-1 quantizations in one launch: the Fprop pair X [T, in] and
  * W [out, in], which share their reduction extent (36Kr, section
  * "Fehlerdiagnoseexperiment": Fprop takes X and W, both quantized along
- * `in`). One persistent grid walks the row groups of A and then of B, which
+ * `in`). One launch covers the row groups of A and then those of B, which
  * saves one launch's ramp and drain.
  *
  *   xa_bf16, rows_a, lda / xb_bf16, rows_b, ldb : the two sources
