@@ -759,6 +759,11 @@ def main():
                 "traffic": recorded_traffic(QUANT_SRC, BLOCK_QUANT_TRAFFIC),
                 "avg_us_per_launch": round(q["us"] / q["launches"], 2),
                 "algorithmic_bytes_per_launch": round(q["bytes"] / q["launches"]),
+                # measured limiter (rocprofv3 SQ_INSTS_VALU / SQ_WAVES of the H32 + RNE
+                # instance): vector-instruction issue, not HBM
+                "limited_by": "VALU issue: 326 VALU instructions per wave (4 cycles each on a "
+                              "16-lane SIMD), issued for 82-93% of the launch "
+                              "(profiles/quant_dual_block_t16384_counters.md)",
             },
             "gemm_all": {"tflops": round(g_all_fl / (g_all_us * 1e-6) / 1e12, 2),
                          "frac": round(g_all_fl / (g_all_us * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4)},
