@@ -748,6 +748,11 @@ def main():
                 "avg_gflop_per_launch": round(dom["flops"] / dom["launches"] / 1e9, 3),
                 "avg_us_per_launch": round(dom["us"] / dom["launches"], 2),
                 "algorithmic_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
+                # measured limiter: the shader clock under this load (in-kernel
+                # s_memtime over s_memrealtime on a timing build of the same kernel)
+                "limited_by": "clock under load: 1.6-1.7 GHz against the 2.4 GHz of the peak; "
+                              "in cycles within 8-10% of an MFMA-only build (profiles/"
+                              "gemm_fprop_q_proj_mfma_counters.md)",
             },
             "quant_roofline": {
                 "kernel": "quant_dual_kernel (both orientations from one read)",
