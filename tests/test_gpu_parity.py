@@ -192,6 +192,37 @@ def test_quantize_dual_matches_oracle_and_single(mx, shape, rot, rnd):
         assert np.array_equal(host_u8(a.scales), host_u8(b.scales))
 
 
+@pytest.mark.parametrize("rot", ROTS)
+@pytest.mark.parametrize("rnd", RNDS)
+def test_quantize_dual_every_bf16_pattern(mx, rot, rnd):
+    """Every bf16 bit pattern (NaN/Inf/subnormal included) through the dual
+    quantizer's fp32 staging, in row blocks (axis 1) and column blocks
+    (axis 0): the 65536 patterns, every pattern again behind a 7.97 anchor,
+    and the special blocks (zeros, overflow inside the butterfly, lone
+    NaN/Inf, subnormal ramps); both outputs against the oracle."""
+    f = np.float32
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    n_anch = -(-65536 // 31)
+    pad = np.zeros(n_anch * 31, np.uint16)
+    pad[:65536] = allv
+    anch = np.concatenate([np.full((n_anch, 1), 0x40FF, np.uint16), pad.reshape(n_anch, 31)], 1)
+    special = f32_to_bf16_bits(np.stack([
+        np.zeros(32, f), np.full(32, -0.0, f), np.full(32, 3.0e38, f),
+        np.where(np.arange(32) % 2 == 0, 3.0e38, -3.0e38).astype(f),
+        np.full(32, 1e-40, f), np.linspace(-1e-39, 1e-39, 32).astype(f),
+        np.r_[np.full(31, 1.0, f), f(np.inf)], np.r_[np.full(31, 1.0, f), f(np.nan)],
+        np.r_[np.full(16, f(np.inf)), np.full(16, -np.inf)].astype(f),
+        np.linspace(-6, 6, 32).astype(f), np.ldexp(np.ones(32, f), np.arange(-16, 16)).astype(f)]))
+    x = np.concatenate([allv.reshape(2048, 32), anch, special], 0)
+    x = np.concatenate([x, np.zeros((-x.shape[0] % 32, 32), np.uint16)], 0)   # rows % 32 == 0
+    x = np.concatenate([x, x[::-1]], 1)      # 64 columns; column blocks mix other patterns
+    s1, s0 = 0x5EED, 0x5EED | (1 << 32)
+    q1, q0 = mx.quantize_dual(to_dev(x), rot, rnd, seed1=s1, seed0=s0)
+    _sync()
+    _check_q(q1, oracle.quantize_ref(x, 1, rotate=rot, rounding=rnd, seed=s1), f"dual axis 1 {rot} {rnd}")
+    _check_q(q0, oracle.quantize_ref(x, 0, rotate=rot, rounding=rnd, seed=s0), f"dual axis 0 {rot} {rnd}")
+
+
 def test_quantize_dual_strided_and_full_size(mx):
     """A row-strided source, and the full-size Fprop activation (8192 x 4096)
     against the single-axis launches."""
