@@ -265,6 +265,75 @@ def _gemm_case(mx, op, a_src, b_src, rot, rnd, seed, check_bf16=True):
     return err
 
 
+def _designed_operand(mx, codes, scales):
+    """A quantized operand built directly from codes [MN, K] and E8M0 scales
+    [MN, K/32] (reduction-major, no rotation), tiled by the oracle's layout
+    functions, as an axis-1 descriptor of a [MN, K] source."""
+    import torch
+    mn, k = codes.shape
+    c = torch.from_numpy(oracle.tile_codes(codes)).cuda()
+    s = torch.from_numpy(oracle.tile_scales(scales, k)).cuda()
+    d = mx.QTensorDesc(c.data_ptr(), s.data_ptr(), mn, k, 1, 32, mx.ROTATE["none"],
+                       mx.ROUND["rne"], 0, mx.FORMATS["fp4_e2m1"])
+    return mx.QTensor(c, s, d)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_exact_on_designed_operands(mx, out_dtype):
+    """Every pair of E2M1 codes (both signs, both zeros) meets in the
+    products, under per-block scales 2^-2 .. 2^2 (A) and 2^-1 .. 2^1 (B)
+    that change from block to block. Every product is a multiple of 2^-5
+    and every partial sum stays below 2^17, so fp32 accumulation in any
+    order is exact: the output must equal the fp64 product exactly (bf16:
+    its nearest-even rounding). Four output tiles, three K slices."""
+    M, N, K = 512, 512, 384
+    m, n, k = np.arange(M)[:, None], np.arange(N)[:, None], np.arange(K)[None, :]
+    kb = np.arange(K // 32)[None, :]
+    ca = ((m * 7 + k) % 16).astype(np.uint8)
+    cb = ((n * 5 + 3 * k) % 16).astype(np.uint8)
+    sa = (125 + (m + kb) % 5).astype(np.uint8)
+    sb = (126 + (3 * n + kb) % 3).astype(np.uint8)
+    qa, qb = _designed_operand(mx, ca, sa), _designed_operand(mx, cb, sb)
+    got = mx.linear("fprop", qa, qb, out_dtype)
+    _sync()
+    ref = oracle.dequantize_ref(ca, sa) @ oracle.dequantize_ref(cb, sb).T
+    assert np.all(np.abs(ref) < 2.0 ** 17)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref)              # exact in fp32
+    if out_dtype == "bf16":
+        import torch
+        g = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, oracle.bf16_round_ref(want))
+    else:
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_gemm_nan_scale_block(mx):
+    """A block whose scale is the NaN code 0xFF (what the quantizers write,
+    with zero codes, for a block holding a NaN or Inf) makes every output
+    that reduces over it NaN, as in the oracle's fp64 product; the rest of
+    C is unaffected."""
+    M, N, K = 256, 256, 256
+    rng = np.random.default_rng(5)
+    ca = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    ca[37, 64:96] = 0
+    sa[37, 2] = 0xFF                      # row 37 of A, block 2
+    cb[200, 224:256] = 0
+    sb[200, 7] = 0xFF                     # row 200 of B (column 200 of C), block 7
+    qa, qb = _designed_operand(mx, ca, sa), _designed_operand(mx, cb, sb)
+    got = mx.linear("fprop", qa, qb, "f32")
+    _sync()
+    ref = oracle.dequantize_ref(ca, sa) @ oracle.dequantize_ref(cb, sb).T
+    g = got.cpu().numpy()
+    assert np.array_equal(np.isnan(g), np.isnan(ref))
+    assert np.isnan(ref[37]).all() and np.isnan(ref[:, 200]).all()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(g[fin], ref[fin].astype(np.float32))       # small exact sums
+
+
 def test_gemm_tiny_wgrad_workload(mx):
     """dY 256x128 and X 256x96, N(0,1), seed 0; H32 + RNE along the 256 tokens;
     dW = dY^T X, 128x96 fp32."""
