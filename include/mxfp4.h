@@ -280,6 +280,8 @@ mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_
  * Both must have the same format (else MX_ERR_MISMATCH): two MXFP8 operands
  * run the E4M3 comparator GEMM (same call, same C), two MXFP4 operands the
  * MXFP4 GEMM.
+ * A block with the NaN scale code 0xFF (a NaN or Inf in its source block)
+ * makes every element of C that reduces over it NaN.
  * Requirements: C aligned to its element size (4 bytes for fp32, 2 for bf16),
  * ldc >= N. M or N == 0 launches nothing; K == 0 with M, N > 0 writes zeros.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN,
