@@ -204,6 +204,39 @@ def test_fp8_gemm_strided_out_and_deterministic(mx, out_dtype):
     assert torch.all(big[:, N:] == -7.0).item()
 
 
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp4_e2m1"])
+def test_gemm_nan_source_block(mx, fmt):
+    """A NaN in one source block of X and an Inf in one of W: the quantizers
+    write that block as scale 0xFF with zero codes, and the GEMM makes the
+    row of C (X) and the column of C (W) that reduce over it NaN, as the
+    oracle's product does; every other element within its bound."""
+    import torch
+    rng = np.random.default_rng(17)
+    X = _rand_bits(rng, (64, 256))
+    W = _rand_bits(rng, (96, 256), 0.05)
+    X[5, 40] = 0x7FC0                                     # NaN in row 5, block 1
+    W[70, 200] = 0x7F80                                   # +Inf in row 70, block 6
+    if fmt == "fp8_e4m3":
+        qa, qb = mx.quantize_fp8(to_dev(X), 1, "hadamard"), mx.quantize_fp8(to_dev(W), 1, "hadamard")
+    else:
+        qa, qb = mx.quantize(to_dev(X), 1, "hadamard"), mx.quantize(to_dev(W), 1, "hadamard")
+    got = mx.linear("fprop", qa, qb, "f32").cpu().numpy()
+    _sync()
+    C_ref, ra, rb = oracle.linear_ref("fprop", X, W, rotate="hadamard", fmt=fmt)
+    assert ra.scales[5, 1] == 0xFF and rb.scales[70, 6] == 0xFF
+    nan = np.isnan(C_ref)
+    assert nan[5].all() and nan[:, 70].all() and nan.sum() == 64 + 96 - 1
+    assert np.array_equal(np.isnan(got), nan)
+    fin = ~nan
+    if fmt == "fp8_e4m3":
+        bound = e4m3_gemm_bound(ra, rb)
+    else:
+        da = np.abs(oracle.dequantize_ref(ra.codes, ra.scales, ra.fmt))
+        db = np.abs(oracle.dequantize_ref(rb.codes, rb.scales, rb.fmt))
+        bound = (256 / 32 + 4) * 2.0 ** -23 * (da @ db.T)
+    assert np.all(np.abs(got[fin].astype(np.float64) - C_ref[fin]) <= bound[fin])
+
+
 def test_fp8_gemm_k_zero_writes_zeros(mx):
     import torch
     A = mx.quantize_fp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), 0)
