@@ -131,7 +131,8 @@ typedef struct mx_qtensor {
  * Byte sizes of the tiled codes and scales of a [rows, cols] source quantized
  * along `axis`, padding included (see mx_qtensor). Host-only; launches nothing.
  * Errors: MX_ERR_NULL (null out-pointer), MX_ERR_ARG (axis, block != 32),
- * MX_ERR_SHAPE (negative extents, or the axis extent not a multiple of 32).
+ * MX_ERR_SHAPE (negative extents, or the axis extent not a multiple of 32),
+ * MX_ERR_UNSUPPORTED (a non-empty source with rows or cols above 2^31).
  */
 mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block,
                             size_t *codes_bytes, size_t *scales_bytes);
@@ -164,7 +165,8 @@ mx_status mx_quantize_sizes(int64_t rows, int64_t cols, int32_t axis, int32_t bl
  * Requirements: ld >= cols; axis 1: x_bf16 16-byte aligned and ld % 8 == 0;
  * axis 0: x_bf16 2-byte aligned (any ld; 4-byte-aligned rows load faster).
  * rows == 0 or cols == 0 is valid and launches nothing.
- * Limit: the padded codes (MNp * Kp / 2 bytes) must stay below 1 GiB, else
+ * Limit: the padded codes (MNp * Kp / 2 bytes) must stay below 1 GiB, rows
+ * and cols at most 2^31, and rows * ld * 2 bytes at most 2^62, else
  * MX_ERR_UNSUPPORTED.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_UNSUPPORTED,
  * MX_ERR_HIP.
@@ -188,9 +190,9 @@ mx_status mx_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld
  *   codes1 / scales1 / desc1 : the axis-1 operand (mx_quantize_sizes with
  *       axis 1 gives the sizes), quantized with seed1.
  *   codes0 / scales0 / desc0 : the axis-0 operand, quantized with seed0.
- *   Ownership, alignment of the outputs, the descriptors (may be NULL) and
- *   the error codes are as for mx_quantize. The results are byte-identical
- *   to the two mx_quantize calls.
+ *   Ownership, alignment of the outputs, the descriptors (may be NULL), the
+ *   limits and the error codes are as for mx_quantize. The results are
+ *   byte-identical to the two mx_quantize calls.
  */
 mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64_t ld,
                            int32_t block, int32_t rotate, int32_t round, uint64_t seed1,
@@ -213,9 +215,9 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
  *   codes_a, scales_a, desc_a / codes_b, scales_b, desc_b : as codes,
  *       scales, out_desc of mx_quantize with axis 1, one set per operand.
  *   Either operand may be empty (rows 0). Ownership, alignment, the
- *   descriptors (may be NULL) and the error codes are as for mx_quantize,
- *   checked for A and then for B before anything is launched. The results
- *   are byte-identical to the two mx_quantize calls.
+ *   descriptors (may be NULL), the limits and the error codes are as for
+ *   mx_quantize, checked for A and then for B before anything is launched.
+ *   The results are byte-identical to the two mx_quantize calls.
  */
 mx_status mx_quantize_pair(const void *xa_bf16, int64_t rows_a, int64_t lda,
                            const void *xb_bf16, int64_t rows_b, int64_t ldb, int64_t cols,
@@ -253,7 +255,8 @@ mx_status mx_quantize_fp8_sizes(int64_t rows, int64_t cols, int32_t axis, int32_
  *          Code = sign << 7 | E4M3 magnitude (exponent bias 7, 0x7E = 448;
  *          0x7F is never written).
  *  scales  as for mx_quantize.
- * Limit: the padded codes (MNp * Kp bytes) must stay below 1 GiB.
+ * Limit: the padded codes (MNp * Kp bytes) must stay below 1 GiB; the other
+ * limits are mx_quantize's.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_UNSUPPORTED,
  * MX_ERR_HIP.
  */
@@ -284,8 +287,11 @@ mx_status mx_quantize_fp8(const void *x_bf16, int64_t rows, int64_t cols, int64_
  * makes every element of C that reduces over it NaN.
  * Requirements: C aligned to its element size (4 bytes for fp32, 2 for bf16),
  * ldc >= N. M or N == 0 launches nothing; K == 0 with M, N > 0 writes zeros.
+ * Limits: each operand's as for mx_quantize (MX_ERR_UNSUPPORTED beyond them,
+ * also for a descriptor not filled by a quantize call), and M * ldc elements
+ * of C at most 2^62 bytes (else MX_ERR_UNSUPPORTED).
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN,
- * MX_ERR_MISMATCH, MX_ERR_HIP.
+ * MX_ERR_MISMATCH, MX_ERR_UNSUPPORTED, MX_ERR_HIP.
  */
 mx_status mx_linear(int32_t op, const mx_qtensor *A, const mx_qtensor *B, void *C,
                     int64_t ldc, int32_t out_dtype, void *stream);
@@ -335,7 +341,8 @@ mx_status mx_linear_batched(int32_t op, int32_t count, const mx_qtensor *A, cons
  * magnitude 2^128 or more (scale codes 126 and 127 only, which the
  * quantizers never write) become +-Inf. Empty operands launch nothing.
  * Errors: MX_ERR_NULL, MX_ERR_ARG, MX_ERR_SHAPE (ld < cols, or q's extents),
- * MX_ERR_ALIGN, MX_ERR_UNSUPPORTED (q's size limit), MX_ERR_HIP.
+ * MX_ERR_ALIGN, MX_ERR_UNSUPPORTED (q's limits, or rows * ld * 4 bytes above
+ * 2^62), MX_ERR_HIP.
  */
 mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *stream);
 

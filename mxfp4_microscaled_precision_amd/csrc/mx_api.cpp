@@ -56,6 +56,22 @@ void padded_extents(int64_t rows, int64_t cols, int32_t axis, int64_t *mnp, int6
 // 256-row block tile past the end must still be representable).
 constexpr int64_t kMaxCodeBytes = (int64_t)1 << 30;
 
+// Larger extents are unsupported: with at least 32 elements along the other
+// axis their codes would pass the limit above anyway, and below it the
+// product of two padded extents cannot overflow int64.
+constexpr int64_t kMaxExtent = (int64_t)1 << 31;
+
+bool extents_too_large(int64_t rows, int64_t cols) {
+  return rows > kMaxExtent || cols > kMaxExtent;
+}
+
+// True when `rows` rows of `ld` elements of `elem_bytes` bytes each span more
+// than 2^62 bytes, which no addressing in the kernels is built for
+// (rows <= kMaxExtent).
+bool span_too_large(int64_t rows, int64_t ld, int64_t elem_bytes) {
+  return rows > 0 && ld > (((int64_t)1 << 62) / elem_bytes) / rows;
+}
+
 mx_status check_qtensor(const mx_qtensor *q) {
   if (q == nullptr) return MX_ERR_NULL;
   if (q->axis != 0 && q->axis != 1) return MX_ERR_ARG;
@@ -69,6 +85,7 @@ mx_status check_qtensor(const mx_qtensor *q) {
   if (q->rows > 0 && q->cols > 0) {
     if (q->codes == nullptr || q->scales == nullptr) return MX_ERR_NULL;
     if (!aligned(q->codes, 16) || !aligned(q->scales, 4)) return MX_ERR_ALIGN;
+    if (extents_too_large(q->rows, q->cols)) return MX_ERR_UNSUPPORTED;
     int64_t mnp, kp;
     padded_extents(q->rows, q->cols, q->axis, &mnp, &kp);
     if (mnp * kp * code_bytes_x2(q->format) / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
@@ -106,6 +123,7 @@ mx_status check_quantize(const void *x_bf16, int64_t rows, int64_t cols, int64_t
   if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return MX_ERR_NULL;
   if (ld < cols) return MX_ERR_SHAPE;
   if (!aligned(codes, 16) || !aligned(scales, 4)) return MX_ERR_ALIGN;
+  if (extents_too_large(rows, cols) || span_too_large(rows, ld, 2)) return MX_ERR_UNSUPPORTED;
   int64_t mnp, kp;
   padded_extents(rows, cols, axis, &mnp, &kp);
   if (mnp * kp * code_bytes_x2(format) / 2 >= kMaxCodeBytes) return MX_ERR_UNSUPPORTED;
@@ -125,6 +143,7 @@ mx_status sizes(int64_t rows, int64_t cols, int32_t axis, int32_t block, int32_t
   if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
   const int64_t k = axis == 1 ? cols : rows;
   if (k % 32 != 0) return MX_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && extents_too_large(rows, cols)) return MX_ERR_UNSUPPORTED;
   int64_t mnp, kp;
   padded_extents(rows, cols, axis, &mnp, &kp);
   *codes_bytes = (size_t)(mnp * kp * code_bytes_x2(format) / 2);
@@ -247,6 +266,7 @@ mx_status mx_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, int64
     if (!aligned(codes1, 16) || !aligned(scales1, 4) || !aligned(codes0, 16) ||
         !aligned(scales0, 4))
       return MX_ERR_ALIGN;
+    if (extents_too_large(rows, cols) || span_too_large(rows, ld, 2)) return MX_ERR_UNSUPPORTED;
     for (int axis = 0; axis < 2; ++axis) {
       int64_t mnp, kp;
       padded_extents(rows, cols, axis, &mnp, &kp);
@@ -303,6 +323,7 @@ mx_status linear_entry(int32_t op, const mx_qtensor *A, const mx_qtensor *B, voi
   if (!*empty) {
     if (C == nullptr) return MX_ERR_NULL;
     if (!aligned(C, out_dtype == MX_OUT_F32 ? 4 : 2)) return MX_ERR_ALIGN;
+    if (span_too_large(M, ldc, out_dtype == MX_OUT_F32 ? 4 : 2)) return MX_ERR_UNSUPPORTED;
   }
   g->a_codes = static_cast<const uint8_t *>(A->codes);
   g->a_scales = static_cast<const uint8_t *>(A->scales);
@@ -361,6 +382,7 @@ mx_status mx_dequantize(const mx_qtensor *q, float *out, int64_t ld, void *strea
   if (q->rows == 0 || q->cols == 0) return MX_OK;
   if (out == nullptr) return MX_ERR_NULL;
   if (!aligned(out, 4)) return MX_ERR_ALIGN;
+  if (span_too_large(q->rows, ld, 4)) return MX_ERR_UNSUPPORTED;
   mx::DequantArgs a;
   a.codes = static_cast<const uint8_t *>(q->codes);
   a.scales = static_cast<const uint8_t *>(q->scales);

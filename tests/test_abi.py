@@ -126,6 +126,33 @@ def test_quantize_rejects_before_launch():
     assert _q(lib, P, -1, 64, 64) == -2
 
 
+def test_quantize_rejects_extents_that_overflow():
+    """Extents whose padded product (or source span) would overflow int64
+    are refused on the host; they used to wrap around the 1 GiB check and
+    reach a launch."""
+    lib = mx.load_library()
+    P = 4096
+    assert _q(lib, P, 1 << 36, 1 << 36, 1 << 36) == -6            # product wraps to 0
+    assert _q(lib, P, 1 << 36, 1 << 36, 1 << 36, axis=0) == -6
+    assert _q(lib, P, (1 << 31) + 32, 64, 64) == -6               # an extent above 2^31
+    assert _q(lib, P, 1 << 20, 64, 1 << 60) == -6                 # rows * ld * 2 above 2^62
+    assert _q(lib, P, 1 << 20, 64, 1 << 60, axis=0) == -6
+    assert _q8(lib, P, 1 << 36, 1 << 36, 1 << 36) == -6
+    assert _qd(lib, P, 1 << 36, 1 << 36, 1 << 36) == -6
+    assert _qd(lib, P, 1 << 20, 64, 1 << 60) == -6
+    assert _qp(lib, P, 1 << 20, 1 << 60, P, 64, 64, 64) == -6
+    assert _qp(lib, P, 64, 64, P, 1 << 36, 64, 64) == -6                 # B rows above 2^31
+    for sizes in (mx.quantize_sizes, mx.quantize_fp8_sizes):
+        with pytest.raises(mx.MxError) as ei:
+            sizes(1 << 36, 1 << 36, 1)
+        assert ei.value.status == -6
+        assert sizes(1 << 40, 0, 1) == (0, 0)                     # empty stays valid
+    # the span limit's edge (2^20 rows of 2^41 bf16 elements = 2^62 bytes): the
+    # largest ld passes it and stops at the next check, a misaligned source
+    assert _q(lib, P + 2, 1 << 20, 64, 1 << 41) == -3
+    assert _q(lib, P + 2, 1 << 20, 64, (1 << 41) + 8) == -6
+
+
 def _qp(lib, xa, ra, lda, xb, rb, ldb, cols, block=32, rot=1, rnd=0, ca=16, sa=16, cb=4096,
         sb=4096, da=None, db=None):
     return lib.mx_quantize_pair(xa, ra, lda, xb, rb, ldb, cols, block, rot, rnd, 5, 6, ca, sa,
@@ -246,6 +273,10 @@ def test_linear_rejects_before_launch():
     assert _lin(lib, 0, X, _desc(96, 128, 1, fmt=1)) == -5
     assert _lin(lib, 0, _desc(64, 128, 1, fmt=1), _desc(96, 128, 1, fmt=1), C=None) == -1
     assert lib.mx_linear(0, None, ctypes.byref(W), 4096, 96, 0, None) == -1
+    # descriptors not filled by a quantize call, with extents that would overflow
+    assert _lin(lib, 0, _desc(1 << 36, 1 << 36, 1), _desc(96, 1 << 36, 1)) == -6
+    assert _lin(lib, 0, X, W, ldc=1 << 60) == -6          # M * ldc * 4 bytes above 2^62
+    assert _lin(lib, 0, X, W, ldc=1 << 60, out=1) == -6
 
 
 def test_linear_empty_is_a_noop():
@@ -300,4 +331,6 @@ def test_dequantize_rejects_before_launch():
     assert deq(_desc(64, 128, 1, codes=None)) == -1
     assert deq(_desc(64, 128, 1, fmt=3)) == -4
     assert deq(_desc(1 << 17, 1 << 14, 1)) == -6          # beyond the size limit
+    assert deq(_desc(1 << 36, 1 << 36, 0)) == -6          # padded product would wrap
+    assert deq(_desc(64, 128, 1), ld=1 << 60) == -6       # rows * ld * 4 bytes above 2^62
     assert deq(_desc(0, 128, 1), out=None) == 0           # empty: nothing launched
