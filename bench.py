@@ -94,15 +94,18 @@ def _dev_bf16(bits, device="cuda"):
 
 
 # ------------------------------------------------------------------ timing
-def settle(fn, min_ms=SETTLE_MS):
+def settle(fn, min_ms=SETTLE_MS, join=None):
     """Run fn(i) back to back for at least min_ms of GPU time (untimed,
-    sized from a short first burst); returns the number of calls."""
+    sized from a short first burst); returns the number of calls. join()
+    makes the current stream wait for work fn left on other streams."""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(3):
         fn(i)
+    if join is not None:
+        join()
     e1.record()
     torch.cuda.synchronize()
     per = max(e0.elapsed_time(e1) / 3, 1e-3)
@@ -113,13 +116,15 @@ def settle(fn, min_ms=SETTLE_MS):
     return 3 + n
 
 
-def timed(fn, steps, warmup=0):
+def timed(fn, steps, warmup=0, join=None):
     """Average ms per call of fn(i): at least SETTLE_MS of calls back to back,
     then `warmup` more, then `steps` calls between one pair of HIP events on
-    the current stream (the stream the library launches on), bracketed by
-    device synchronisation. Returns (ms per call, wall ms per call)."""
+    the current stream, bracketed by device synchronisation. A call may
+    launch on other streams if it first makes them wait for the current one;
+    join() then makes the current stream wait for them before the closing
+    event. Returns (ms per call, wall ms per call)."""
     import torch
-    settle(fn)
+    settle(fn, join=join)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -129,6 +134,8 @@ def timed(fn, steps, warmup=0):
     e0.record()
     for i in range(steps):
         fn(i)
+    if join is not None:
+        join()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -139,7 +146,18 @@ def timed(fn, steps, warmup=0):
 class BlockRunner:
     """The 7 linears of one Llama-3.1-8B block at T tokens, resident on the
     GPU with their quantized operands and outputs; pre-marshalled C-ABI
-    calls (no torch calls inside a step)."""
+    calls (no torch compute inside a step; torch only records and waits on
+    HIP events).
+
+    A step of the dual-quantizer schedule runs on two streams of default
+    priority: the quantizations on one, in group order, and the GEMMs on the
+    other, each group's GEMMs waiting for that group's quantizations, and
+    each group's quantizations waiting for that group's GEMMs of the step
+    before (they overwrite the operands those read). The quantizer of the
+    next group can then start while a GEMM drains its last tiles, and a GEMM
+    while the last quantizer workgroups finish. Same launches, same
+    outputs; `overlap = False` (and the per-launch instrumented pass) runs
+    them in order on the current stream."""
 
     def __init__(self, mx, tokens=16384, keep_host=("k_proj",)):
         import torch
@@ -147,6 +165,9 @@ class BlockRunner:
         self.mx = mx
         self.lib = mx.load_library()
         self.stream = torch.cuda.current_stream().cuda_stream
+        self.side = (torch.cuda.Stream(), torch.cuda.Stream())   # quantizer, GEMM streams
+        self.overlap = True
+        self.plan = None
         self.T = tokens
         wls = block_workloads(tokens)
         self.variants = wls[0].variants
@@ -303,12 +324,56 @@ class BlockRunner:
                                           lib.mx_quantize, qargs(k, axis)))
                     calls.append(gemm(L, op, a, b, odt))
         self.calls = calls
+        self.plan = None if per_op else self._two_stream_plan(calls)
         return calls
 
+    def _two_stream_plan(self, calls):
+        """Per group: (its quantizer calls on the quantizer stream, its GEMM
+        calls on the GEMM stream, quantized event, GEMMs-done event)."""
+        import torch
+        qs, gs = (s.cuda_stream for s in self.side)
+        plan = []
+        for kind, _, fn, args in calls:
+            if kind == "quant_dual":
+                if not plan or plan[-1][1]:
+                    plan.append(([], [], torch.cuda.Event(), torch.cuda.Event()))
+                plan[-1][0].append((fn, tuple(args[:-1]) + (qs,)))
+            else:
+                plan[-1][1].append((fn, tuple(args[:-1]) + (gs,)))
+        self._gemms_recorded = False
+        return plan
+
     def step(self, i=0):
-        for kind, _, fn, args in self.calls:
-            if fn(*args):
-                raise RuntimeError(f"library call {fn.__name__} failed")
+        if self.plan is None or not self.overlap:
+            for kind, _, fn, args in self.calls:
+                if fn(*args):
+                    raise RuntimeError(f"library call {fn.__name__} failed")
+            return
+        import torch
+        qs, gs = self.side
+        cur = torch.cuda.current_stream()
+        qs.wait_stream(cur)
+        gs.wait_stream(cur)
+        for duals, gemms, quantized, gemms_done in self.plan:
+            if self._gemms_recorded:
+                qs.wait_event(gemms_done)
+            for fn, args in duals:
+                if fn(*args):
+                    raise RuntimeError(f"library call {fn.__name__} failed")
+            quantized.record(qs)
+            gs.wait_event(quantized)
+            for fn, args in gemms:
+                if fn(*args):
+                    raise RuntimeError(f"library call {fn.__name__} failed")
+            gemms_done.record(gs)
+        self._gemms_recorded = True
+
+    def join(self):
+        """Make the current stream wait for everything the steps launched."""
+        import torch
+        cur = torch.cuda.current_stream()
+        for s in self.side:
+            cur.wait_stream(s)
 
     def instrumented(self, steps):
         """`steps` steps with a HIP event before every launch and after the
@@ -346,15 +411,20 @@ def block_bench(mx, args):
     res = {}
     for label in [head] + [lb for lb in labels if lb != head]:
         br.build(label)
-        ms, wall = timed(br.step, args.steps, args.warmup)
+        ms, wall = timed(br.step, args.steps, args.warmup, join=br.join)
         res[label] = {"ms_per_step": ms, "wall_ms_per_step": wall,
                       "tflops": flops / (ms * 1e-3) / 1e12}
         print(f"[bench] block {label}: {ms:.3f} ms/step, {res[label]['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
-    # per-launch split of the headline variant
+    # the headline variant with every launch in order on one stream
     calls = br.build(head)
-    settle(br.step)
+    br.overlap = False
+    ms, _ = timed(br.step, args.steps, args.warmup)
+    res[head]["serial_ms_per_step"] = ms
+    print(f"[bench] block {head}, one stream: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    # per-launch split of the headline variant (in order, one stream)
     per_launch, inst_ms = br.instrumented(args.steps)
+    br.overlap = True
     split = {}
     per_op = {}
     for (kind, info, _, _), ms in zip(calls, per_launch):
@@ -728,7 +798,8 @@ def main():
                 "workload": (f"Llama-3.1-8B block T={br.T}: 7 linears x Fprop/Dgrad/Wgrad "
                              f"(21 MXFP4 GEMMs; k/v ops and gate/up Dgrad and Wgrad as grouped "
                              f"launches), {head}, each of X/W/dY quantized once "
-                             f"into both orientations"),
+                             f"into both orientations; quantizations and GEMMs on two "
+                             f"streams, each group's GEMMs after its quantizations"),
                 "tokens": br.T, "variant": head, "gemms": 21,
                 "gflop_per_step": round(flops / 1e9, 1),
                 "launches_per_step": len(br.calls),
@@ -773,13 +844,17 @@ def main():
             "gemm_all": {"tflops": round(g_all_fl / (g_all_us * 1e-6) / 1e12, 2),
                          "frac": round(g_all_fl / (g_all_us * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4)},
             # the step's time split over the kernel classes in proportion to
-            # their event-timed durations (so the split sums to ms_per_step);
-            # the raw event-timed sums are per_kernel_us_events: an event
-            # between every two launches adds a few us to each
+            # their event-timed durations in the one-stream pass (so the split
+            # sums to ms_per_step); the raw event-timed sums are
+            # per_kernel_us_events: an event between every two launches adds a
+            # few us to each
             "per_kernel_us": {k: round(v["us"] * h["ms_per_step"] / inst_ms, 1)
                               for k, v in split.items()},
             "per_kernel_us_events": {k: round(v["us"], 1) for k, v in split.items()},
             "instrumented_ms_per_step": round(inst_ms, 5),
+            # the same launches in order on one stream (no overlap between a
+            # GEMM's last tiles and the next quantizer)
+            "serial_ms_per_step": round(h["serial_ms_per_step"], 5),
             "per_op": per_op,
             "variants": {lb: {"ms_per_step": round(v["ms_per_step"], 5),
                               "tflops": round(v["tflops"], 2),
