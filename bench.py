@@ -354,6 +354,8 @@ class BlockRunner:
         cur = torch.cuda.current_stream()
         qs.wait_stream(cur)
         gs.wait_stream(cur)
+        if not self._gemms_recorded:
+            qs.wait_stream(gs)     # GEMMs of an earlier plan may still read the operands
         for duals, gemms, quantized, gemms_done in self.plan:
             if self._gemms_recorded:
                 qs.wait_event(gemms_done)
