@@ -9,11 +9,13 @@ operand rotated by the 32-point Hadamard and quantized to MXFP4 (E8M0 scale
 per 32 elements, E2M1 elements, round to nearest even).
 
 One step is one training step's linear-layer work of the block, with the
-inputs already resident in HBM: for each linear, X, W and dY are each
-quantized once into both packed orientations (mx_quantize_dual), then Fprop
-(bf16 out), Dgrad (bf16 out) and Wgrad (fp32 out) run on those operands.
+inputs already resident in HBM: each distinct X, W and dY is quantized once
+into both packed orientations (mx_quantize_dual; q, k and v read one input
+activation X, gate and up another, as in the model), then each linear's
+Fprop (bf16 out), Dgrad (bf16 out) and Wgrad (fp32 out) run on those
+operands.
 `value` is the 21 GEMMs' 2*M*N*K over the step time, i.e. TFLOP/s including
-the Hadamard and the quantization. The block's working set (about 8 GB)
+the Hadamard and the quantization. The block's working set (about 7 GB)
 exceeds the 256 MB last-level cache many times over, so every step reads
 its inputs from HBM.
 
@@ -161,7 +163,7 @@ class BlockRunner:
 
     def __init__(self, mx, tokens=16384, keep_host=("k_proj",)):
         import torch
-        from datagen import LLAMA_BLOCK_LINEARS, block_workloads, workload_tensors
+        from datagen import BLOCK_INPUT_OF, LLAMA_BLOCK_LINEARS, block_workloads, workload_tensors
         self.mx = mx
         self.lib = mx.load_library()
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -178,12 +180,22 @@ class BlockRunner:
             t = workload_tensors(wl)
             if lin.name in keep_host:
                 self.host[lin.name] = t
-            src = {k: _dev_bf16(t[k]) for k in ("X", "W", "dY")}
+            # a linear that reads another's input (k, v: q's; up: gate's)
+            # takes that linear's X and its packed buffers (BLOCK_INPUT_OF)
+            lead = BLOCK_INPUT_OF.get(lin.name)
+            src = {k: _dev_bf16(t[k]) for k in ("X", "W", "dY") if not (lead and k == "X")}
             del t
             bufs = {}
+            if lead:
+                L0 = [L for L in self.lins if L["name"] == lead][0]
+                src = {"X": L0["src"]["X"], **src}
+                for axis in (1, 0):
+                    bufs["X", axis] = L0["bufs"]["X", axis][:2] + (mx.QTensorDesc(),)
             for k, x in src.items():
                 rows, cols = x.shape
                 for axis in (1, 0):
+                    if (k, axis) in bufs:
+                        continue
                     cb, sb = mx.quantize_sizes(rows, cols, axis)
                     bufs[k, axis] = (torch.empty(cb, dtype=torch.uint8, device="cuda"),
                                      torch.empty(sb, dtype=torch.uint8, device="cuda"),
@@ -193,7 +205,7 @@ class BlockRunner:
                     "dgrad": torch.empty((T, i), dtype=torch.bfloat16, device="cuda"),
                     "wgrad": torch.empty((o, i), dtype=torch.float32, device="cuda")}
             self.lins.append({"name": lin.name, "out": o, "in": i, "src": src, "bufs": bufs,
-                              "outs": outs})
+                              "outs": outs, "x_of": lead})
             print(f"[bench] block {lin.name}: {T}x{i} -> {o} resident", file=sys.stderr,
                   flush=True)
         # Linears that see their inputs together share one grouped GEMM launch
@@ -283,10 +295,22 @@ class BlockRunner:
                                             mx.OUT_DTYPES[odt], st))
 
         if not per_op:
+            # a shared X is quantized once, by the first linear that reads it;
+            # the others' descriptors describe those buffers as that call does
+            for L in self.lins:
+                if L["x_of"]:
+                    x = L["src"]["X"]
+                    for axis, sd in ((1, seeds["X"][0]), (0, seeds["X"][1])):
+                        c, s, d = L["bufs"]["X", axis]
+                        d.codes, d.scales = c.data_ptr(), s.data_ptr()
+                        d.rows, d.cols = x.shape
+                        d.axis, d.block, d.rotate, d.round, d.seed = axis, 32, R, D, sd
+                        d.format = mx.FORMATS["fp4_e2m1"]
             for grp in self.groups:
                 for L in grp["lins"]:
                     for k in ("X", "W", "dY"):
-                        calls.append(dual(L, k))
+                        if not (k == "X" and L["x_of"]):
+                            calls.append(dual(L, k))
                 names = tuple(L["name"] for L in grp["lins"])
                 for op, a, b, odt in self.OPS:
                     if op in self.GROUPED_OPS.get(names, ()):
@@ -799,9 +823,10 @@ def main():
             "config": {
                 "workload": (f"Llama-3.1-8B block T={br.T}: 7 linears x Fprop/Dgrad/Wgrad "
                              f"(21 MXFP4 GEMMs; k/v ops and gate/up Dgrad and Wgrad as grouped "
-                             f"launches), {head}, each of X/W/dY quantized once "
-                             f"into both orientations; quantizations and GEMMs on two "
-                             f"streams, each group's GEMMs after its quantizations"),
+                             f"launches), {head}; q/k/v read one input activation and "
+                             f"gate/up another, as in the model; each distinct X, W and dY "
+                             f"quantized once into both orientations; quantizations and GEMMs "
+                             f"on two streams, each group's GEMMs after its quantizations"),
                 "tokens": br.T, "variant": head, "gemms": 21,
                 "gflop_per_step": round(flops / 1e9, 1),
                 "launches_per_step": len(br.calls),

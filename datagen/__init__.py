@@ -45,6 +45,7 @@ __all__ = [
     "Workload",
     "LinearShape",
     "LLAMA_BLOCK_LINEARS",
+    "BLOCK_INPUT_OF",
     "workload",
     "WORKLOADS",
 ]
@@ -120,6 +121,11 @@ LLAMA_BLOCK_LINEARS: Tuple[LinearShape, ...] = (
     LinearShape("down_proj", 4096, 14336),
 )
 
+# Linears that read another linear's input activation in the block: q, k and
+# v project the same normalised hidden state, gate and up the same one after
+# the attention. The follower's X is the leader's tensor.
+BLOCK_INPUT_OF: Dict[str, str] = {"k_proj": "q_proj", "v_proj": "q_proj", "up_proj": "gate_proj"}
+
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
@@ -128,7 +134,9 @@ class Workload:
     op: "fprop" (Y = X W^T), "dgrad" (dX = dY W) or "wgrad" (dW = dY^T X).
     tensors: name -> (rows, cols, kind) in draw order; kind is one of
       "act" (N(0,1) + outliers), "act_plain" (N(0,1)), "weight" (N(0,0.02^2)),
-      "grad" (1e-4 * t_3).
+      "grad" (1e-4 * t_3). A fifth entry, in chunked workloads only, is the
+      data seed that tensor is drawn with instead of the workload's (a tensor
+      shared with another workload).
     """
     name: str
     op: str
@@ -136,7 +144,7 @@ class Workload:
     out_features: int
     in_features: int
     data_seed: int
-    tensors: Tuple[Tuple[str, int, int, str], ...]
+    tensors: Tuple[tuple, ...]
     variants: Tuple[Tuple[str, str, str, int], ...]  # (label, rotate, round, seed)
     out_dtype: str = "f32"
     chunk_rows: int = 0      # > 0: chunked multi-stream recipe (module docstring)
@@ -226,8 +234,11 @@ def workload_tensors(w: Workload) -> Dict[str, np.ndarray]:
     stream, or (chunk_rows > 0) chunk by chunk from per-chunk streams."""
     if w.chunk_rows > 0:
         with ThreadPoolExecutor(_gen_threads()) as pool:
-            return {name: _draw_chunked(w.data_seed, t, r, c, kind, w.chunk_rows, pool)
-                    for t, (name, r, c, kind) in enumerate(w.tensors)}
+            return {spec[0]: _draw_chunked(spec[4] if len(spec) > 4 else w.data_seed, t,
+                                           spec[1], spec[2], spec[3], w.chunk_rows, pool)
+                    for t, spec in enumerate(w.tensors)}
+    if any(len(spec) > 4 for spec in w.tensors):
+        raise ValueError("a per-tensor data seed needs a chunked workload")
     rng = np.random.Generator(np.random.PCG64(w.data_seed))
     return {name: _draw(rng, r, c, kind) for (name, r, c, kind) in w.tensors}
 
@@ -269,13 +280,19 @@ BLOCK_VARIANTS = (
 def block_workloads(tokens: int = BLOCK_TOKENS) -> List[Workload]:
     """All 21 GEMMs of one Llama-3.1-8B block (7 linears x fprop/dgrad/wgrad).
 
-    Each linear draws its own X (T x in, with outliers), W (out x in) and
-    dY (T x out) with data seed 5 * 100 + linear index, in row chunks of
-    CHUNK_ROWS (the chunked recipe of the module docstring).
+    Each linear draws its own W (out x in) and dY (T x out) with data seed
+    5 * 100 + linear index, in row chunks of CHUNK_ROWS (the chunked recipe
+    of the module docstring). X (T x in, with outliers) is the block's input
+    activation of that linear: q, k and v share the one drawn with q's seed,
+    gate and up the one drawn with gate's (BLOCK_INPUT_OF); o and down draw
+    their own. X is tensor 0 of every linear, so a shared X is the same
+    array.
     """
     out: List[Workload] = []
+    index = {lin.name: li for li, lin in enumerate(LLAMA_BLOCK_LINEARS)}
     for li, lin in enumerate(LLAMA_BLOCK_LINEARS):
-        tensors = (("X", tokens, lin.in_features, "act"),
+        x_seed = 500 + index[BLOCK_INPUT_OF.get(lin.name, lin.name)]
+        tensors = (("X", tokens, lin.in_features, "act", x_seed),
                    ("W", lin.out_features, lin.in_features, "weight"),
                    ("dY", tokens, lin.out_features, "grad"))
         for op in ("fprop", "dgrad", "wgrad"):
