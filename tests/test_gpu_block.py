@@ -8,7 +8,8 @@ AMD durchbricht die bestehende Erkenntnis ...", section
 "Fehlerdiagnoseexperiment": the three GEMMs of every linear, the
 deterministic rotation against its two randomized comparators.
 
-Each linear's X, W and dY are quantized as the benchmark's step quantizes
+Each linear's X (q, k and v read one input activation, gate and up another,
+as in the model), W and dY are quantized as the benchmark's step quantizes
 them: once into both orientations (mx_quantize_dual), seeds by role (A of an
 op s, B s | 1 << 32). For every op:
   * the dual outputs equal the two single-orientation launches byte for byte;
